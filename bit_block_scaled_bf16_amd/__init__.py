@@ -1,0 +1,145 @@
+"""NVFP4 quantizer and NVFP4 GEMM for AMD MI355X (gfx950).
+
+Python side of the C-ABI library libnvfp4.so. ``_lib`` holds the entry points
+with their C names (explicit output tensors); the helpers here allocate the
+outputs with torch (device memory only) and call them. Every computation runs
+in the library's HIP kernels; if the library is missing, importing the
+binding's entry points raises.
+
+The method: gist.science summary of "Pretraining Large Language Models with
+NVFP4" (Resumen técnico §2) -- 16-element blocks with E4M3 scales and an FP32
+tensor scale, 16x16 weight blocks, stochastic rounding of gradients, a 16x16
+random Hadamard transform of the weight-gradient inputs, NVFP4 GEMMs.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from . import _lib
+from ._lib import (  # noqa: F401  (re-exported constants and raw entry points)
+    BF16,
+    BLOCK_1D,
+    BLOCK_2D,
+    F32,
+    OUT_COL,
+    OUT_ROW,
+    ROUND_RN,
+    ROUND_SR,
+    Nvfp4Error,
+    nvfp4_dequantize,
+    nvfp4_gemm,
+    nvfp4_philox_fill,
+    nvfp4_quantize,
+    nvfp4_rht_quantize,
+    nvfp4_rht_sign_mask,
+    nvfp4_rht_transform,
+)
+
+__all__ = [
+    "NVFP4Tensor",
+    "quantize",
+    "rht_quantize",
+    "dequantize",
+    "gemm",
+    "load",
+]
+
+
+def load():
+    """Loads libnvfp4.so (raises ImportError when it has not been built)."""
+    return _lib.lib()
+
+
+@dataclass
+class NVFP4Tensor:
+    """One stored orientation of an NVFP4 matrix [rows][cols] (device)."""
+
+    codes: "object"         # uint8 [rows, cols/2]
+    scales: "object"        # uint8 [rows, cols/16] (1D) or [rows/16, cols/16] (2D)
+    tensor_scale: "object"  # float32 [4]; element 0 is S
+    block: int              # BLOCK_1D or BLOCK_2D
+    rows: int
+    cols: int
+
+
+def _empty(shape, dtype, device):
+    import torch
+
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _scalar(device):
+    import torch
+
+    return torch.zeros(4, dtype=torch.float32, device=device)
+
+
+def quantize(x, block: int = BLOCK_1D, rounding: int = ROUND_RN, seed: int = 0, offset: int = 0,
+             outputs: int = OUT_ROW | OUT_COL, amax=None, dev_status=None):
+    """Quantizes x [rows, cols] (bf16 or float32, device).
+
+    Returns (row copy or None, column copy or None, amax workspace or None).
+    The column copy is stored as the quantized transpose [cols, rows/2].
+    """
+    import torch
+
+    rows, cols = x.shape
+    dev = x.device
+    scale = _scalar(dev)
+    ws = None if amax is not None else _scalar(dev)
+    row = col = None
+    q_row = s_row = q_col = s_col = None
+    two_d = block == BLOCK_2D
+    if outputs & OUT_ROW:
+        q_row = _empty((rows, cols // 2), torch.uint8, dev)
+        s_row = _empty((rows // 16, cols // 16) if two_d else (rows, cols // 16), torch.uint8, dev)
+        row = NVFP4Tensor(q_row, s_row, scale, block, rows, cols)
+    if outputs & OUT_COL:
+        q_col = _empty((cols, rows // 2), torch.uint8, dev)
+        s_col = _empty((cols // 16, rows // 16) if two_d else (cols, rows // 16), torch.uint8, dev)
+        col = NVFP4Tensor(q_col, s_col, scale, block, cols, rows)
+    nvfp4_quantize(x, block, rounding, seed, offset, outputs, amax, ws, q_row, s_row, q_col,
+                   s_col, scale, dev_status)
+    return row, col, ws
+
+
+def rht_quantize(x, rht_seed: int, rounding: int = ROUND_RN, seed: int = 0, offset: int = 0,
+                 amax=None, dev_status=None):
+    """Hadamard transform along tokens + 16x1 quantization of x [tokens, cols].
+
+    Returns (NVFP4Tensor [cols, tokens], amax workspace or None).
+    """
+    import torch
+
+    tokens, cols = x.shape
+    dev = x.device
+    scale = _scalar(dev)
+    ws = None if amax is not None else _scalar(dev)
+    q = _empty((cols, tokens // 2), torch.uint8, dev)
+    s = _empty((cols, tokens // 16), torch.uint8, dev)
+    nvfp4_rht_quantize(x, rht_seed, rounding, seed, offset, amax, ws, q, s, scale, dev_status)
+    return NVFP4Tensor(q, s, scale, BLOCK_1D, cols, tokens), ws
+
+
+def dequantize(t: NVFP4Tensor, out_dtype=None):
+    """Float32 (default) or bf16 values of an NVFP4 tensor."""
+    import torch
+
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    y = _empty((t.rows, t.cols), out_dtype, t.codes.device)
+    nvfp4_dequantize(t.codes, t.scales, t.tensor_scale, t.rows, t.cols, t.block, y)
+    return y
+
+
+def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=None, out=None):
+    """C = deq(a) @ deq(b)^T, float32 accumulation, bf16 output by default."""
+    import torch
+
+    if a.cols != b.cols:
+        raise ValueError("a and b must share K")
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    c = out if out is not None else _empty((a.rows, b.rows), out_dtype, a.codes.device)
+    nvfp4_gemm(a.codes, a.scales, a.tensor_scale, a.block, b.codes, b.scales, b.tensor_scale,
+               b.block, a.rows, b.rows, a.cols, c)
+    return c

@@ -1,0 +1,218 @@
+// Device-side building blocks of the NVFP4 kernels (gfx950).
+//
+// Number formats (gist.science summary of "Pretraining Large Language Models
+// with NVFP4", Resumen técnico §2 "Formato NVFP4"): 4-bit E2M1 elements, E4M3
+// block scales, an FP32 tensor scale. The exact rounding rules are the
+// library's definitions stated in include/nvfp4.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// ---------------------------------------------------------------------------
+// Scalars of the two-level scaling.
+// ---------------------------------------------------------------------------
+
+// Largest E2M1 magnitude times largest E4M3 value: the tensor amax maps to
+// the top of both ranges.
+constexpr float kTensorScaleDivisor = 2688.0f;
+// Tensor scales below 2^-100 are replaced by 1 (the tensor quantizes to 0).
+constexpr float kTensorScaleFloor = 7.888609052210118e-31f;  // 2^-100
+
+// float32 tensor decode scale from the tensor amax.
+__device__ __forceinline__ float tensor_scale_from_amax(float amax) {
+  float s = __fdiv_rn(amax, kTensorScaleDivisor);
+  return (s < kTensorScaleFloor) ? 1.0f : s;  // also maps amax == 0 to 1
+}
+
+// E4M3FN byte nearest to t (t >= 0, finite), ties to even mantissa,
+// saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_from_float(float t) {
+  if (t >= 448.0f) return 0x7Eu;
+  const uint32_t u = __float_as_uint(t);
+  if (u < 0x3C800000u) {  // t < 2^-6: subnormal grid m * 2^-9 (m == 8 is 2^-6)
+    return static_cast<uint32_t>(__builtin_rintf(t * 512.0f));
+  }
+  // keep 3 mantissa bits, round to nearest even, then rebias 127 -> 7
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  return (r >> 20) - (120u << 3);
+}
+
+// Value of an E4M3FN byte (never called with the NaN bytes).
+__device__ __forceinline__ float e4m3_to_float(uint32_t b) {
+  const uint32_t e = (b >> 3) & 0xFu;
+  const uint32_t m = b & 7u;
+  if (e == 0) return static_cast<float>(m) * 0.001953125f;  // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Block scale and encode multiplier for a block with amax a_b.
+struct BlockScale {
+  uint32_t byte;  // E4M3 scale byte
+  float mult;     // 1 / (s_f * S), 0 when the scale is 0 (block quantizes to 0)
+};
+
+__device__ __forceinline__ BlockScale block_scale(float amax_b, float six_s, float s) {
+  BlockScale bs;
+  bs.byte = e4m3_from_float(__fdiv_rn(amax_b, six_s));
+  const float sf = e4m3_to_float(bs.byte);
+  bs.mult = (bs.byte == 0u) ? 0.0f : __fdiv_rn(1.0f, __fmul_rn(sf, s));
+  return bs;
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 rounding.
+// ---------------------------------------------------------------------------
+
+// Two round-to-nearest-even E2M1 codes (a in the low nibble, b in the high
+// nibble) written into byte `sel` of `old`. gfx950's converter with scale
+// 1.0 implements exactly the rounding of include/nvfp4.h: nearest, ties to
+// the even code, saturation at 6, the sign bit of the input kept (checked
+// against the CPU definition over every float near every tie, and by the
+// parity tests).
+template <int sel>
+__device__ __forceinline__ uint32_t cvt_pk_e2m1_rn(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, sel);
+}
+
+// Eight RN codes packed into one 32-bit word, element j in nibble j.
+__device__ __forceinline__ uint32_t pack8_rn(const float* y) {
+  uint32_t w = 0;
+  w = cvt_pk_e2m1_rn<0>(w, y[0], y[1]);
+  w = cvt_pk_e2m1_rn<1>(w, y[2], y[3]);
+  w = cvt_pk_e2m1_rn<2>(w, y[4], y[5]);
+  w = cvt_pk_e2m1_rn<3>(w, y[6], y[7]);
+  return w;
+}
+
+// Stochastically rounded E2M1 code of y from 16 random bits u16: with
+// a = min(|y|, 6), lo the largest magnitude <= a and hi the next one, round
+// up exactly when u16 / 2^16 < (a - lo) / (hi - lo). The comparison is done
+// on integers / exact floats, so it is exact.
+__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
+  const uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
+  const float a = fminf(fabsf(y), 6.0f);
+  const uint32_t u = __float_as_uint(a);
+  uint32_t code;
+  if (u >= 0x3F800000u) {
+    // a >= 1: magnitude code is exponent:top mantissa bit; the 22 bits below
+    // are (a - lo) / step * 2^22
+    code = (u >> 22) - 252u;
+    code += ((u16 << 6) < (u & 0x3FFFFFu)) ? 1u : 0u;
+  } else if (u >= 0x3F000000u) {
+    // 0.5 <= a < 1: lo = 0.5, step 0.5, fraction = 23 mantissa bits
+    code = 1u + (((u16 << 7) < (u & 0x7FFFFFu)) ? 1u : 0u);
+  } else {
+    // a < 0.5: lo = 0, step 0.5, fraction = 2a
+    code = (static_cast<float>(u16) < a * 131072.0f) ? 1u : 0u;
+  }
+  return code | sign;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11).
+// ---------------------------------------------------------------------------
+
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+struct U4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U4 philox4x32_10(uint32_t k0, uint32_t k1, U4 c) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * c.x;
+    const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c.z;
+    const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
+    const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
+    c = U4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  return c;
+}
+
+// Random words for the 8 elements of group g (element 2i uses the low half
+// of word i, element 2i+1 the high half).
+__device__ __forceinline__ U4 sr_words(uint32_t k0, uint32_t k1, uint64_t g, uint32_t offset,
+                                       uint32_t stream) {
+  return philox4x32_10(k0, k1,
+                       U4{static_cast<uint32_t>(g), static_cast<uint32_t>(g >> 32), offset, stream});
+}
+
+// Eight SR codes for y[0..7] from one Philox block.
+__device__ __forceinline__ uint32_t pack8_sr(const float* y, U4 w) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t u16 = (ws[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    out |= e2m1_sr(y[j], u16) << (4 * j);
+  }
+  return out;
+}
+
+constexpr uint32_t kStreamRow = 0;
+constexpr uint32_t kStreamCol = 1;
+
+// ---------------------------------------------------------------------------
+// Loads.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// |x| as ordered integer bits (float32 layout): larger bits = larger |x|,
+// NaN above infinity.
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// ---------------------------------------------------------------------------
+// 16-point Hadamard transform (Sylvester order) of the signed values, in
+// float32 with a fixed butterfly order: pair distances 1, 2, 4, 8, each
+// mapping (a, b) -> (a + b, a - b), then a multiply by 1/4 (exact).
+// sign_mask bit i set means the input i is negated first.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((sign_mask >> i) & 1u) << 31));
+  }
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = __fadd_rn(a, b);
+        v[i + h] = __fsub_rn(a, b);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __fmul_rn(v[i], 0.25f);
+}
+
+// Exchange with the neighbouring lane (lane ^ 1) through DPP.
+__device__ __forceinline__ uint32_t swap_adjacent_lanes(uint32_t v) {
+  // quad_perm [1, 0, 3, 2]
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+}
+
+// Maximum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64));
+    v = (o > v) ? o : v;
+  }
+  return v;
+}
+
+}  // namespace nvfp4

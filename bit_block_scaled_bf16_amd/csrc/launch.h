@@ -1,0 +1,59 @@
+// Internal interface between the C ABI (argument checking, abi.cpp) and the
+// kernel launchers (*.hip). Arguments reaching a launcher are already valid.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+struct QuantizeLaunch {
+  const void* x;
+  bool x_bf16;
+  int64_t rows, cols, ldx;  // for the RHT path rows are tokens
+  bool block_2d;
+  bool rht;
+  bool sr;
+  uint64_t seed;
+  uint32_t offset;
+  uint32_t sign_mask;  // RHT signs (bit i: d_i = -1)
+  int outputs;         // 1 = row copy, 2 = column copy (RHT path: column copy)
+  const float* amax_in;
+  float* amax_ws;
+  uint8_t *q_row, *s_row, *q_col, *s_col;
+  float* tensor_scale;
+  int32_t* dev_status;
+};
+
+// Each returns 0, or -1 when a launch failed.
+int launch_quantize(const QuantizeLaunch& q, hipStream_t stream);
+
+int launch_dequantize(const uint8_t* q, const uint8_t* s, const float* tensor_scale, int64_t rows,
+                      int64_t cols, bool block_2d, bool out_bf16, void* y, int64_t ldy,
+                      hipStream_t stream);
+
+struct GemmLaunch {
+  const uint8_t *qa, *sa;
+  const float* ta;
+  bool a_2d;
+  const uint8_t *qb, *sb;
+  const float* tb;
+  bool b_2d;
+  int64_t M, N, K;
+  void* c;
+  bool c_bf16;
+  int64_t ldc;
+};
+
+int launch_gemm(const GemmLaunch& g, hipStream_t stream);
+
+int launch_philox_fill(uint64_t seed, uint32_t c2, uint32_t c3, int64_t n_groups, uint32_t* out,
+                       hipStream_t stream);
+
+int launch_rht_transform(const void* x, bool x_bf16, int64_t tokens, int64_t cols, int64_t ldx,
+                         uint32_t sign_mask, float* out, hipStream_t stream);
+
+// Host-side Philox4x32-10 (same definition as the device function).
+void philox4x32_10_host(uint32_t k0, uint32_t k1, const uint32_t ctr[4], uint32_t out[4]);
+
+}  // namespace nvfp4

@@ -1,0 +1,217 @@
+/*
+ * nvfp4.h -- C ABI of the NVFP4 quantizer and NVFP4 GEMM for AMD MI355X
+ * (gfx950).
+ *
+ * NVFP4 stores a tensor as 4-bit E2M1 codes (two per byte), one E4M3 scale
+ * byte per block of 16 elements (1x16, 16x1) or per 16x16 tile, and one FP32
+ * tensor scale. The format and the training recipe come from NVIDIA's report
+ * "Pretraining Large Language Models with NVFP4" as summarised on
+ * gist.science (Resumen técnico §2: "Formato NVFP4" -- 16-element blocks, E4M3
+ * block scale, FP32 tensor scale; "Transformadas de Hadamard Aleatorias
+ * (RHT)" -- 16x16 Hadamard transform with a fixed random sign vector on the
+ * weight-gradient inputs; "Escalado Bidimensional (2D) y Redondeo
+ * Estocástico" -- 16x16 weight blocks, stochastic rounding of gradients;
+ * "Precisión Mixta Selectiva" -- the GEMMs run on NVFP4 operands).
+ *
+ * Numerics (the pages give none; these are the library's definitions, all in
+ * float32 with round-to-nearest-even unless stated):
+ *   A   = max |x| over the tensor (after the transform on the RHT path)
+ *   S   = A / 2688   (2688 = 6 * 448); S := 1 when A / 2688 < 2^-100
+ *   per block: s_b = E4M3_rne_sat(a_b / (6 * S)); s_f = value(s_b)
+ *              r = 1 / (s_f * S), or every code 0 when s_f == 0
+ *   per element: y = x * r; q = E2M1 round-to-nearest-even (ties to the code
+ *              with mantissa bit 0, |y| > 6 -> 6, sign bit of y kept), or
+ *              stochastic: a = min(|y|, 6), round up to the next magnitude
+ *              exactly when u16 / 2^16 < (a - lo) / (hi - lo)
+ *   u16 for element e (row-major index of the stored matrix): Philox4x32-10
+ *              with key (seed lo, seed hi), counter (e>>3 lo, e>>3 hi,
+ *              offset, stream), word (e&7)>>1, half e&1 (0 = low 16 bits);
+ *              stream 0 = row-blocked copy, 1 = column-blocked copy
+ *   RHT of 16 consecutive tokens x of one column: x' = (1/4) H (d .* x),
+ *              H the Sylvester 16x16 Hadamard matrix (H[i][j] =
+ *              (-1)^popcount(i&j)), d_i = 1 - 2 * bit i of word 0 of
+ *              Philox4x32-10(key = rht_seed, counter (0, 0, 0, 2))
+ *   dequant:   x_hat = (e2m1(q) * s_f) * S
+ *
+ * Layouts (all row-major, dense, owned by the caller):
+ *   codes: byte j of a row holds element 2j (low nibble) and 2j+1 (high).
+ *   row-blocked copy of an R x C matrix:    codes [R][C/2], scales [R][C/16]
+ *   column-blocked copy (16x1 blocks), stored as the quantized transpose:
+ *                                            codes [C][R/2], scales [C][R/16]
+ *   16x16 blocks: codes [R][C/2] and [C][R/2] (transposed), scale grid
+ *                 [R/16][C/16] and its transpose [C/16][R/16].
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer except the host-side ones named so is a DEVICE pointer
+ *     owned by the caller; the library never allocates, frees or keeps
+ *     pointers, and keeps no state between calls (thread-safe).
+ *   - Work is enqueued on `stream` and the call returns without waiting.
+ *   - Argument errors are detected on the host before any HIP call and
+ *     returned synchronously; nothing is enqueued then.
+ *   - Device pointers must be 16-byte aligned; leading dimensions in
+ *     elements must keep every row 16-byte aligned.
+ *   - Data-dependent conditions never synchronise: a non-finite tensor amax
+ *     stores 1 into *dev_status (when dev_status is not NULL); the outputs
+ *     are then unspecified. The library never writes 0 there.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,  /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2, /* a size or leading dimension is invalid */
+  NVFP4_ERR_ENUM = 3,  /* unknown enum value or unsupported combination */
+  NVFP4_ERR_ALIGN = 4, /* a pointer or row is not 16-byte aligned */
+  NVFP4_ERR_HIP = 5    /* a kernel launch failed (hipGetLastError) */
+};
+
+/* Element types of inputs and outputs. */
+enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 };
+/* Block shapes. */
+enum { NVFP4_BLOCK_1D = 0, NVFP4_BLOCK_2D = 1 };
+/* Rounding of the elements. */
+enum { NVFP4_ROUND_RN = 0, NVFP4_ROUND_SR = 1 };
+/* Output orientations (bit mask). */
+enum { NVFP4_OUT_ROW = 1, NVFP4_OUT_COL = 2 };
+
+/*
+ * nvfp4_quantize -- two-level NVFP4 quantization of an R x C matrix.
+ * (gist.science summary, Resumen técnico §2 "Formato NVFP4"; for 16x16 blocks
+ * §2 "Escalado Bidimensional (2D) y Redondeo Estocástico".)
+ *
+ *   x          [rows][ldx] input, x_dtype NVFP4_F32 or NVFP4_BF16.
+ *   rows, cols  >= 0. cols % 16 == 0. rows % 16 == 0 when NVFP4_OUT_COL is
+ *               requested or block == NVFP4_BLOCK_2D. rows == 0 or cols == 0
+ *               is an empty tensor: only *tensor_scale (= 1) and *amax_ws
+ *               (= 0) are written.
+ *   ldx         >= cols.
+ *   block       NVFP4_BLOCK_1D: row copy in 1x16 blocks along cols, column
+ *               copy in 16x1 blocks along rows. NVFP4_BLOCK_2D: 16x16 tiles,
+ *               one scale each; the column copy holds the transposed codes,
+ *               which dequantize to exactly the transpose of the row copy.
+ *   rounding    NVFP4_ROUND_RN or NVFP4_ROUND_SR (SR with BLOCK_2D is
+ *               NVFP4_ERR_ENUM: the recipe rounds weights to nearest).
+ *   seed, offset  Philox key and counter word 2 for SR (ignored for RN).
+ *   outputs     non-empty mask of NVFP4_OUT_ROW / NVFP4_OUT_COL; both are
+ *               produced from one read of x and share the tensor scale.
+ *   amax_in     NULL, or 1 float: the tensor amax to use instead of
+ *               computing it (e.g. from an earlier pass).
+ *   amax_ws     1 float of workspace, required when amax_in is NULL; holds
+ *               the computed amax afterwards.
+ *   q_row, s_row  row copy codes [rows][cols/2] and scales [rows][cols/16]
+ *               (1D) or grid [rows/16][cols/16] (2D); required with OUT_ROW.
+ *   q_col, s_col  column copy codes [cols][rows/2] and scales [cols][rows/16]
+ *               (1D) or grid^T [cols/16][rows/16] (2D); required with OUT_COL.
+ *   tensor_scale  out: 1 float, S (decode scale) for dequantize and GEMM.
+ *   dev_status    NULL or 1 int32, set to 1 on a non-finite amax.
+ */
+int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                   int block, int rounding, uint64_t seed, uint32_t offset, int outputs,
+                   const float* amax_in, float* amax_ws, uint8_t* q_row, uint8_t* s_row,
+                   uint8_t* q_col, uint8_t* s_col, float* tensor_scale, int32_t* dev_status,
+                   hipStream_t stream);
+
+/*
+ * nvfp4_rht_quantize -- weight-gradient operand path: 16-point random
+ * Hadamard transform along the token dimension, then 16x1 NVFP4 blocks along
+ * tokens, stored transposed so the token dimension is the GEMM K dimension.
+ * (gist.science summary, Resumen técnico §2 "Transformadas de Hadamard
+ * Aleatorias (RHT)" and "... Redondeo Estocástico"; news.hamidun.com,
+ * "Cómo Funciona".)
+ *
+ *   x          [tokens][ldx], x_dtype NVFP4_F32 or NVFP4_BF16.
+ *   tokens     >= 0, multiple of 16. cols >= 0, multiple of 16. ldx >= cols.
+ *   rht_seed   selects the fixed sign vector d (same seed on both operands
+ *              of one weight-gradient GEMM).
+ *   rounding, seed, offset  as nvfp4_quantize (stream word 1).
+ *   amax_in    NULL or 1 float: amax of the transformed tensor.
+ *   amax_ws    1 float, required when amax_in is NULL (holds the amax of the
+ *              transformed tensor afterwards).
+ *   q_t        codes [cols][tokens/2]; s_t scales [cols][tokens/16].
+ *   tensor_scale, dev_status  as nvfp4_quantize.
+ */
+int nvfp4_rht_quantize(const void* x, int x_dtype, int64_t tokens, int64_t cols, int64_t ldx,
+                       uint64_t rht_seed, int rounding, uint64_t seed, uint32_t offset,
+                       const float* amax_in, float* amax_ws, uint8_t* q_t, uint8_t* s_t,
+                       float* tensor_scale, int32_t* dev_status, hipStream_t stream);
+
+/*
+ * nvfp4_dequantize -- y = (e2m1(q) * s_f) * S for one stored orientation.
+ * (Implied by the format, gist.science summary, Resumen técnico §2 "Formato
+ * NVFP4".)
+ *
+ *   q          codes [rows][cols/2]; s scales [rows][cols/16] (BLOCK_1D) or
+ *              [rows/16][cols/16] (BLOCK_2D, rows % 16 == 0).
+ *   tensor_scale  1 float, S.
+ *   rows, cols >= 0, cols % 16 == 0.
+ *   out_dtype  NVFP4_F32, or NVFP4_BF16 (round to nearest even of the
+ *              float32 value).
+ *   y          [rows][ldy], ldy >= cols.
+ */
+int nvfp4_dequantize(const uint8_t* q, const uint8_t* s, const float* tensor_scale,
+                     int64_t rows, int64_t cols, int block, int out_dtype, void* y, int64_t ldy,
+                     hipStream_t stream);
+
+/*
+ * nvfp4_gemm -- C[M][N] = deq(A) . deq(B)^T with A [M][K] and B [N][K]
+ * NVFP4 matrices blocked along K, float32 accumulation.
+ * (gist.science summary, Resumen técnico §2 "Precisión Mixta Selectiva": the
+ * linear-layer GEMMs run on NVFP4 operands.)
+ *
+ *   qa, sa, ta  A codes [M][K/2], scales [M][K/16] (a_block BLOCK_1D) or
+ *               [M/16][K/16] (BLOCK_2D, M % 16 == 0), tensor scale (1 float).
+ *   qb, sb, tb  B likewise with N.
+ *   M, N >= 0; K >= 0, K % 16 == 0. K == 0 writes zeros.
+ *   c           [M][ldc], ldc >= N; c_dtype NVFP4_BF16 (round to nearest
+ *               even) or NVFP4_F32. C = (ta * tb) * sum_k a_k b_k, where
+ *               a_k = e2m1 * s_f (exact), accumulated in float32. c needs
+ *               only the alignment of its element type, and ldc any value
+ *               >= N (the 16-byte rule does not apply to C).
+ */
+int nvfp4_gemm(const uint8_t* qa, const uint8_t* sa, const float* ta, int a_block,
+               const uint8_t* qb, const uint8_t* sb, const float* tb, int b_block, int64_t M,
+               int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc, hipStream_t stream);
+
+/* ---- Inspection hooks used by the parity tests ---- */
+
+/*
+ * nvfp4_philox_fill -- out[4g .. 4g+3] = Philox4x32-10(key = (seed lo,
+ * seed hi), counter = (g lo, g hi, c2, c3)) for g in [0, n_groups): the same
+ * device function the stochastic rounding uses. out holds 4 * n_groups
+ * uint32. n_groups >= 0.
+ */
+int nvfp4_philox_fill(uint64_t seed, uint32_t c2, uint32_t c3, int64_t n_groups, uint32_t* out,
+                      hipStream_t stream);
+
+/*
+ * nvfp4_rht_transform -- out[t][c] = the float32 transformed values that
+ * nvfp4_rht_quantize quantizes (same device code), for inspection.
+ * x as nvfp4_rht_quantize; out is dense [tokens][cols] float32.
+ */
+int nvfp4_rht_transform(const void* x, int x_dtype, int64_t tokens, int64_t cols, int64_t ldx,
+                        uint64_t rht_seed, float* out, hipStream_t stream);
+
+/*
+ * nvfp4_rht_sign_mask -- host-only: bit i set means d_i = -1 for rht_seed.
+ * Touches no device.
+ */
+uint32_t nvfp4_rht_sign_mask(uint64_t rht_seed);
+
+/* Host-only: static description of a status code. */
+const char* nvfp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -120,11 +120,12 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
 
 
 def quantize_rows(m, s: np.float32, rounding: str = "rn", seed: int = 0, offset: int = 0,
-                  stream: int = STREAM_ROW):
+                  stream: int = STREAM_ROW, index_base: int = 0):
     """Steps 3-7 for a float32 matrix m [R, C] with 1x16 blocks along C.
 
     Returns (codes [R, C] unpacked uint8, scale bytes [R, C/16]).
-    For SR the element index is the row-major index of m.
+    For SR the element index is ``index_base`` plus the row-major index of m
+    (index_base lets a caller quantize a few rows of a larger stored matrix).
     """
     m = np.asarray(m, dtype=np.float32)
     r_, c_ = m.shape
@@ -136,7 +137,7 @@ def quantize_rows(m, s: np.float32, rounding: str = "rn", seed: int = 0, offset:
     y = (blocks * r[:, :, None]).astype(np.float32)
     u16 = None
     if rounding == "sr":
-        e = np.arange(r_ * c_, dtype=np.int64).reshape(r_, c_ // 16, 16)
+        e = (np.int64(index_base) + np.arange(r_ * c_, dtype=np.int64)).reshape(r_, c_ // 16, 16)
         u16 = sr_random_u16(seed, offset, stream, e)
     codes = _round_codes(y, rounding, u16)
     codes = np.where(nz[:, :, None], codes, np.uint8(0)).astype(np.uint8)

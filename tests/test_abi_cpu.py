@@ -1,0 +1,148 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every entry point
+that include/nvfp4.h declares, derives the Hadamard sign vector on the host
+exactly as the oracle does, and rejects bad arguments before any HIP call
+(so none of these calls touches a GPU)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as o
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from bit_block_scaled_bf16_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libnvfp4.so is not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|uint32_t|const char\*)\s+(nvfp4_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("nvfp4_quantize", "nvfp4_dequantize", "nvfp4_rht_quantize", "nvfp4_gemm"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from bit_block_scaled_bf16_amd import _lib
+
+    names = declared_functions()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_sign_mask_matches_oracle(L):
+    for seed in (0, 1, 7, 12345, 2 ** 40 + 3, 2 ** 64 - 1):
+        mask = int(L.nvfp4_rht_sign_mask(seed))
+        d = o.rht_signs(seed)
+        want = sum(1 << i for i in range(16) if d[i] < 0)
+        assert mask == want, seed
+
+
+def test_status_strings(L):
+    for code in range(6):
+        assert L.nvfp4_status_string(code)
+    assert L.nvfp4_status_string(99) == b"unknown status"
+
+
+# A fake, 16-byte aligned "device" address: every call below must be rejected
+# by the host-side checks before anything dereferences it.
+FAKE = 0x10000
+MIS = 0x10008  # 8-byte aligned only
+
+
+def q(L, **kw):
+    a = dict(x=FAKE, x_dtype=1, rows=32, cols=32, ldx=32, block=0, rounding=0, seed=0, offset=0,
+             outputs=3, amax_in=None, amax_ws=FAKE, q_row=FAKE, s_row=FAKE, q_col=FAKE,
+             s_col=FAKE, tensor_scale=FAKE, dev_status=None, stream=None)
+    a.update(kw)
+    return L.nvfp4_quantize(*a.values())
+
+
+def test_quantize_argument_errors(L):
+    assert q(L, x_dtype=7) == 3
+    assert q(L, block=2) == 3
+    assert q(L, rounding=2) == 3
+    assert q(L, outputs=0) == 3 and q(L, outputs=4) == 3
+    assert q(L, block=1, rounding=1) == 3          # SR on 16x16 weight blocks
+    assert q(L, cols=24, ldx=24) == 2               # cols % 16
+    assert q(L, rows=24) == 2                       # column copy needs rows % 16
+    assert q(L, rows=-1) == 2
+    assert q(L, ldx=16) == 2                        # ldx < cols
+    assert q(L, block=1, rows=24, outputs=1) == 2   # 2D needs rows % 16
+    assert q(L, x=None) == 1
+    assert q(L, tensor_scale=None) == 1
+    assert q(L, amax_in=None, amax_ws=None) == 1
+    assert q(L, q_col=None) == 1
+    assert q(L, outputs=1, s_row=None) == 1
+    assert q(L, x=MIS) == 4
+    assert q(L, ldx=36) == 4                        # bf16 rows of 72 bytes
+    assert q(L, q_row=MIS) == 4
+    assert q(L, x_dtype=0, ldx=34) == 4             # fp32 rows of 136 bytes
+
+
+def test_rht_quantize_argument_errors(L):
+    def r(**kw):
+        a = dict(x=FAKE, x_dtype=1, tokens=32, cols=32, ldx=32, rht_seed=7, rounding=1, seed=7,
+                 offset=0, amax_in=None, amax_ws=FAKE, q_t=FAKE, s_t=FAKE, tensor_scale=FAKE,
+                 dev_status=None, stream=None)
+        a.update(kw)
+        return L.nvfp4_rht_quantize(*a.values())
+
+    assert r(tokens=24) == 2
+    assert r(cols=40, ldx=40) == 2
+    assert r(rounding=5) == 3
+    assert r(q_t=None) == 1
+    assert r(amax_ws=None) == 1
+    assert r(s_t=MIS) == 4
+
+
+def test_dequantize_and_gemm_argument_errors(L):
+    d = lambda **kw: L.nvfp4_dequantize(*dict(dict(q=FAKE, s=FAKE, ts=FAKE, rows=32, cols=32,
+                                                   block=0, out=0, y=FAKE, ldy=32, st=None),
+                                              **kw).values())
+    assert d(cols=20, ldy=20) == 2
+    assert d(ldy=16) == 2
+    assert d(block=1, rows=8) == 2
+    assert d(block=9) == 3
+    assert d(out=3) == 3
+    assert d(y=None) == 1
+    assert d(q=MIS) == 4
+    g = lambda **kw: L.nvfp4_gemm(*dict(dict(qa=FAKE, sa=FAKE, ta=FAKE, ab=0, qb=FAKE, sb=FAKE,
+                                             tb=FAKE, bb=0, M=32, N=32, K=32, c=FAKE, cd=1,
+                                             ldc=32, st=None), **kw).values())
+    assert g(K=40) == 2
+    assert g(ldc=16) == 2
+    assert g(ab=1, M=40) == 2
+    assert g(bb=1, N=24) == 2
+    assert g(ab=3) == 3
+    assert g(cd=2) == 3
+    assert g(c=None) == 1
+    assert g(qa=None) == 1
+    assert g(c=FAKE + 1) == 4        # bf16 output needs 2-byte alignment only
+    assert g(cd=0, c=FAKE + 2) == 4  # float32 output needs 4-byte alignment
+    assert g(qa=MIS) == 4
+    # empty products enqueue nothing and succeed
+    assert g(M=0) == 0 and g(N=0) == 0
+
+
+def test_hook_argument_errors(L):
+    assert L.nvfp4_philox_fill(1, 0, 0, -1, FAKE, None) == 2
+    assert L.nvfp4_philox_fill(1, 0, 0, 4, None, None) == 1
+    assert L.nvfp4_philox_fill(1, 0, 0, 0, None, None) == 0
+    assert L.nvfp4_rht_transform(FAKE, 1, 24, 32, 32, 7, FAKE, None) == 2
+    assert L.nvfp4_rht_transform(FAKE, 1, 32, 32, 32, 7, None, None) == 1

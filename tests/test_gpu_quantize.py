@@ -1,0 +1,266 @@
+"""GPU parity of nvfp4_quantize (1x16 / 16x1 / 16x16, RN and SR) with the
+CPU oracle: scale bytes, codes, tensor scale and amax bit for bit.
+
+Sizes are small enough for the oracle to finish in seconds while spanning
+several 256 x 128 workgroup tiles and ragged tile tails; the full-size
+workloads are checked on sampled rows and columns.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as o
+import workloads as wl
+from tests._helpers import announce, host, require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def run_quantize(x_np, dtype, block=0, rounding=0, seed=0, offset=0, outputs=3, amax=None):
+    torch = require_gpu()
+    import bit_block_scaled_bf16_amd as nv
+
+    x = to_device(x_np, dtype)
+    amax_t = None
+    if amax is not None:
+        amax_t = torch.tensor([amax, 0, 0, 0], dtype=torch.float32, device="cuda")
+    row, col, ws = nv.quantize(x, block=block, rounding=rounding, seed=seed, offset=offset,
+                               outputs=outputs, amax=amax_t)
+    torch.cuda.synchronize()
+    return row, col, ws
+
+
+def check_against_oracle(x_np, dtype, rounding="rn", seed=0, offset=0, outputs=("row", "col"),
+                         amax=None):
+    mask = (1 if "row" in outputs else 0) | (2 if "col" in outputs else 0)
+    row, col, ws = run_quantize(x_np, dtype, 0, 0 if rounding == "rn" else 1, seed, offset, mask,
+                                amax)
+    ref = o.quantize(x_np, rounding=rounding, seed=seed, offset=offset, outputs=outputs, amax=amax)
+    some = row if row is not None else col
+    s_gpu = host(some.tensor_scale)[0]
+    first = next(iter(ref.values()))
+    assert s_gpu.view(np.uint32) == np.float32(first.tensor_scale).view(np.uint32)
+    if ws is not None:
+        assert host(ws)[0].view(np.uint32) == np.float32(first.amax).view(np.uint32)
+    if row is not None:
+        assert np.array_equal(host(row.scales), ref["row"].scales)
+        assert np.array_equal(host(row.codes), ref["row"].codes)
+    if col is not None:
+        assert np.array_equal(host(col.scales), ref["col"].scales)
+        assert np.array_equal(host(col.codes), ref["col"].codes)
+
+
+def test_fp32_outlier_matrix_rn_round_trip():
+    """fp32 256x1024, N(0,1), 0.1% outliers x50, 1x16 RN + dequant."""
+    torch = require_gpu()
+    import bit_block_scaled_bf16_amd as nv
+
+    x = wl.fp32_outlier_matrix()
+    announce("fp32 256x1024 RN")
+    check_against_oracle(x, "fp32", outputs=("row",))
+    row, _, _ = run_quantize(x, "fp32", outputs=1)
+    ref = o.quantize(x, outputs=("row",))["row"]
+    deq = host(nv.dequantize(row))
+    want = o.dequantize(ref.codes, ref.scales, ref.tensor_scale)
+    assert np.array_equal(deq.view(np.uint32), want.view(np.uint32))
+    deq16 = host(nv.dequantize(row, torch.bfloat16).float())
+    want16 = torch.from_numpy(want).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(deq16, want16)
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (48, 160), (272, 400), (528, 272)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_dual_rn_ragged_tiles(shape, dtype):
+    announce(f"dual RN {shape} {dtype}")
+    x = wl.normal(shape, seed=shape[0] + shape[1], outlier_channels=min(4, shape[1] // 16),
+                  dtype=dtype)
+    check_against_oracle(x, dtype)
+
+
+@pytest.mark.parametrize("outputs", [("row",), ("col",)])
+def test_single_orientation(outputs):
+    x = wl.activation(272, 400, seed=11)
+    announce(f"single {outputs}")
+    check_against_oracle(x, "bf16", outputs=outputs)
+
+
+def test_row_only_needs_no_row_multiple_of_16():
+    x = wl.normal((37, 64), seed=3)
+    announce("row-only 37x64")
+    check_against_oracle(x, "bf16", outputs=("row",))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_sr_bit_exact(dtype):
+    x = wl.laplace((272, 400), seed=5, dtype=dtype)
+    announce(f"SR {dtype}")
+    check_against_oracle(x, dtype, rounding="sr", seed=7, offset=3)
+    check_against_oracle(x, dtype, rounding="sr", seed=(1 << 40) + 9, offset=0xFFFFFFFF)
+
+
+def test_caller_supplied_amax():
+    x = wl.activation(256, 256, seed=12)
+    announce("amax_in")
+    a = float(np.max(np.abs(x)))
+    check_against_oracle(x, "bf16", amax=a)
+    # a smaller amax saturates blocks; still bit-exact with the same definition
+    check_against_oracle(x, "bf16", amax=a / 3)
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (272, 400), (512, 384)])
+def test_2d_weight_blocks(shape):
+    announce(f"2D {shape}")
+    x = wl.weight(*shape, seed=4)
+    row, col, _ = run_quantize(x, "bf16", block=1, outputs=3)
+    ref = o.quantize_2d(x)
+    assert np.array_equal(host(row.scales), ref["row"].scales)
+    assert np.array_equal(host(col.scales), ref["col"].scales)
+    assert np.array_equal(host(row.codes), ref["row"].codes)
+    assert np.array_equal(host(col.codes), ref["col"].codes)
+    # W and W^T decode to transposes of each other, bit for bit
+    import bit_block_scaled_bf16_amd as nv
+
+    d = host(nv.dequantize(row))
+    dt = host(nv.dequantize(col))
+    assert np.array_equal(d.T, dt)
+
+
+def test_golden_blocks_on_gpu():
+    import json, os
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_blocks.json")))
+    case = g["row_case"]
+    x = np.concatenate([np.array(b["values"], dtype=np.float32) for b in case["blocks"]])[None, :]
+    announce("golden")
+    for dtype in ("fp32",):
+        row, _, _ = run_quantize(x, dtype, outputs=1)
+        assert [int(v) for v in host(row.scales)[0]] == [int(b["scale"], 16) for b in case["blocks"]]
+        codes = o.unpack_codes(host(row.codes))[0]
+        assert codes.tolist() == sum((b["codes"] for b in case["blocks"]), [])
+
+
+def test_rn_sweep_of_ties_through_the_kernel():
+    """Every float32 within 600 ulps of each E2M1 tie and grid point, fed
+    through the full kernel with S = 1 and block multiplier 1 (each 16-block
+    holds a 6.0 and the tensor holds 2688), so y == x."""
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    pts = np.asarray(ties, dtype=np.float32).view(np.int32)
+    k = np.arange(-600, 601, dtype=np.int32)
+    vals = (pts[:, None] + k[None, :]).reshape(-1).view(np.float32)
+    vals = vals[np.abs(vals) <= 6.0]
+    vals = np.concatenate([vals, -vals, np.float32([0.0, -0.0, 1e-40, -1e-40])])
+    nblk = -(-len(vals) // 15)
+    body = np.zeros(nblk * 15, np.float32)
+    body[: len(vals)] = vals
+    blocks = np.concatenate([np.full((nblk, 1), 6.0, np.float32), body.reshape(nblk, 15)], axis=1)
+    flat = blocks.reshape(-1)
+    cols = 256
+    rows = -(-(len(flat) + 16) // cols)
+    rows += (-rows) % 16
+    x = np.zeros(rows * cols, np.float32)
+    x[:16] = np.float32(2688.0)
+    x[16:16 + len(flat)] = flat
+    x = x.reshape(rows, cols)
+    announce(f"tie sweep {x.shape}")
+    check_against_oracle(x, "fp32", outputs=("row",))
+
+
+def test_zero_tiny_and_empty_tensors():
+    torch = require_gpu()
+    import bit_block_scaled_bf16_amd as nv
+
+    for v in (0.0, -0.0, 1e-31):
+        x = np.full((32, 64), v, np.float32)
+        announce(f"constant {v}")
+        check_against_oracle(x, "fp32")
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    row, col, ws = nv.quantize(x, outputs=1)
+    assert host(row.tensor_scale)[0] == 1.0 and host(ws)[0] == 0.0
+
+
+def test_non_finite_amax_sets_status():
+    torch = require_gpu()
+    import bit_block_scaled_bf16_amd as nv
+
+    x = np.zeros((32, 32), np.float32)
+    x[5, 7] = np.inf
+    status = torch.zeros(4, dtype=torch.int32, device="cuda")
+    nv.quantize(to_device(x, "fp32"), dev_status=status)
+    assert host(status)[0] == 1
+    status.zero_()
+    nv.quantize(to_device(np.ones((32, 32), np.float32), "fp32"), dev_status=status)
+    assert host(status)[0] == 0
+
+
+def test_deterministic_repeat():
+    x = wl.laplace((512, 256), seed=9)
+    announce("determinism")
+    r1, c1, _ = run_quantize(x, "bf16", rounding=1, seed=7)
+    r2, c2, _ = run_quantize(x, "bf16", rounding=1, seed=7)
+    assert np.array_equal(host(r1.codes), host(r2.codes))
+    assert np.array_equal(host(c1.codes), host(c2.codes))
+
+
+def test_leading_dimension():
+    torch = require_gpu()
+    import bit_block_scaled_bf16_amd as nv
+
+    big = wl.normal((64, 200), seed=21)
+    x = to_device(big, "bf16")[:, :160]  # ldx = 200 (400 bytes, 16-aligned)
+    announce("ldx")
+    row, col, _ = nv.quantize(x)
+    ref = o.quantize(np.ascontiguousarray(big[:, :160]))
+    assert np.array_equal(host(row.codes), ref["row"].codes)
+    assert np.array_equal(host(col.codes), ref["col"].codes)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, checked on sampled rows / columns.
+# ---------------------------------------------------------------------------
+
+
+def _sampled_rows_check(x, row, col, s, rows_idx, cols_idx):
+    """Row copy on sampled rows, column copy on sampled columns, given S."""
+    for r in rows_idx:
+        codes, sb = o.quantize_rows(x[r:r + 1], s)
+        assert np.array_equal(host(row.codes[r:r + 1]), o.pack_codes(codes)), r
+        assert np.array_equal(host(row.scales[r:r + 1]), sb), r
+    xt = x[:, cols_idx].T.copy()
+    codes, sb = o.quantize_rows(xt, s)
+    assert np.array_equal(host(col.codes[cols_idx]), o.pack_codes(codes))
+    assert np.array_equal(host(col.scales[cols_idx]), sb)
+
+
+def test_full_activation_dual_rn():
+    """bf16 8192x5120, N(0,1) + 16 outlier channels x20, row and column
+    copies in one pass; sampled rows and columns checked bit for bit."""
+    x = wl.activation()
+    announce("full activation 8192x5120")
+    row, col, ws = run_quantize(x, "bf16", outputs=3)
+    a = np.float32(np.max(np.abs(x)))
+    s = o.tensor_scale(a)
+    assert host(ws)[0] == a
+    assert host(row.tensor_scale)[0] == s
+    rng = np.random.default_rng(0)
+    _sampled_rows_check(x, row, col, s, rng.choice(x.shape[0], 24, replace=False),
+                        np.sort(rng.choice(x.shape[1], 48, replace=False)))
+
+
+def test_full_weight_2d():
+    """bf16 20480x5120 weight, N(0, 0.02^2), 16x16 blocks, both orientations;
+    sampled 16-row bands checked bit for bit, W^T identity on a band."""
+    x = wl.weight()
+    announce("full weight 20480x5120")
+    row, col, _ = run_quantize(x, "bf16", block=1, outputs=3)
+    a = np.float32(np.max(np.abs(x)))
+    rng = np.random.default_rng(1)
+    grid_row = host(row.scales)
+    grid_col = host(col.scales)
+    assert np.array_equal(grid_row.T, grid_col)
+    for band in rng.choice(x.shape[0] // 16, 6, replace=False):
+        sl = slice(16 * band, 16 * band + 16)
+        ref = o.quantize_2d(x[sl], amax=a)
+        assert np.array_equal(host(row.codes[sl]), ref["row"].codes)
+        assert np.array_equal(grid_row[band:band + 1], ref["row"].scales)
+        colcodes = host(col.codes[:, 8 * band: 8 * band + 8])
+        assert np.array_equal(colcodes, ref["col"].codes)
