@@ -1,0 +1,264 @@
+"""Benchmark: one NVFP4 linear-layer step (fprop + weight gradient) on one GPU.
+
+Workload (synthetic stand-ins for a linear layer of the 12B hybrid model of
+"Pretraining Large Language Models with NVFP4"): X bf16 [16384, 5120]
+N(0,1) with 16 outlier channels x20, W bf16 [20480, 5120] N(0, 0.02^2),
+dY bf16 [16384, 20480] Laplace(0, 1e-3). One step runs the whole hot path:
+
+  1. nvfp4_quantize(X)        tensor amax + 1x16 RN, row copy  (fprop A)
+  2. nvfp4_quantize(W)        tensor amax + 16x16 RN, W and W^T (fprop B)
+  3. nvfp4_rht_quantize(dY)   RHT amax + RHT + 16x1 SR (Philox seed 7)
+  4. nvfp4_rht_quantize(X)    RHT amax + RHT + 16x1 RN
+  5. nvfp4_gemm fprop         Y  [16384, 20480] = X W^T,  K = 5120,  bf16
+  6. nvfp4_gemm wgrad         dW [20480, 5120] = dY^T X,  K = 16384, bf16
+
+Prints one JSON line. `value` is the step's effective GEMM rate: the two
+GEMMs' 2*M*N*K flops divided by the whole step time (quantizers included).
+Per-call times come from HIP events recorded on the stream the library uses
+(torch's current stream) inside the timed region. `cpu_baseline` times the
+CPU oracle on a bounded slice of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 quantize GB/s (% HBM peak) + NVFP4 GEMM TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 MFMA, MI355X
+
+TOKENS, HIDDEN, FFN = 16384, 5120, 20480
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tokens", type=int, default=TOKENS)
+    return ap.parse_args()
+
+
+class Step:
+    """Pre-allocated operands and outputs of one linear-layer step."""
+
+    def __init__(self, torch, nv, x_np, w_np, dy_np):
+        self.torch, self.nv = torch, nv
+        dev = "cuda"
+        u8 = torch.uint8
+        t, h = x_np.shape
+        f = w_np.shape[0]
+        self.t, self.h, self.f = t, h, f
+        bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+        self.x, self.w, self.dy = bf(x_np), bf(w_np), bf(dy_np)
+        sc = lambda: torch.zeros(4, dtype=torch.float32, device=dev)
+        e = lambda *s: torch.empty(s, dtype=u8, device=dev)
+        # X row copy (fprop A)
+        self.qx, self.sx, self.tx, self.ax = e(t, h // 2), e(t, h // 16), sc(), sc()
+        # W 16x16: W and W^T codes, grid and grid^T
+        self.qw, self.sw, self.qwt, self.swt = e(f, h // 2), e(f // 16, h // 16), e(h, f // 2), e(h // 16, f // 16)
+        self.tw, self.aw = sc(), sc()
+        # RHT copies (wgrad operands), stored [cols][tokens/2]
+        self.qdy, self.sdy, self.tdy, self.ady = e(f, t // 2), e(f, t // 16), sc(), sc()
+        self.qxt, self.sxt, self.txt, self.axt = e(h, t // 2), e(h, t // 16), sc(), sc()
+        self.y = torch.empty((t, f), dtype=torch.bfloat16, device=dev)
+        self.dw = torch.empty((f, h), dtype=torch.bfloat16, device=dev)
+        self.status = torch.zeros(4, dtype=torch.int32, device=dev)
+        self.offset = 0
+
+    def calls(self):
+        nv = self.nv
+        s = self
+        return [
+            ("quantize_x_1x16", lambda: nv.nvfp4_quantize(
+                s.x, nv.BLOCK_1D, nv.ROUND_RN, 0, 0, nv.OUT_ROW, None, s.ax, s.qx, s.sx, None,
+                None, s.tx, s.status)),
+            ("quantize_w_16x16", lambda: nv.nvfp4_quantize(
+                s.w, nv.BLOCK_2D, nv.ROUND_RN, 0, 0, nv.OUT_ROW | nv.OUT_COL, None, s.aw, s.qw,
+                s.sw, s.qwt, s.swt, s.tw, s.status)),
+            ("rht_quantize_dy_sr", lambda: nv.nvfp4_rht_quantize(
+                s.dy, 7, nv.ROUND_SR, 7, s.offset, None, s.ady, s.qdy, s.sdy, s.tdy, s.status)),
+            ("rht_quantize_x_rn", lambda: nv.nvfp4_rht_quantize(
+                s.x, 7, nv.ROUND_RN, 0, 0, None, s.axt, s.qxt, s.sxt, s.txt, s.status)),
+            ("gemm_fprop", lambda: nv.nvfp4_gemm(
+                s.qx, s.sx, s.tx, nv.BLOCK_1D, s.qw, s.sw, s.tw, nv.BLOCK_2D, s.t, s.f, s.h,
+                s.y)),
+            ("gemm_wgrad", lambda: nv.nvfp4_gemm(
+                s.qdy, s.sdy, s.tdy, nv.BLOCK_1D, s.qxt, s.sxt, s.txt, nv.BLOCK_1D, s.f, s.h,
+                s.t, s.dw)),
+        ]
+
+    def work(self):
+        """Algorithmic bytes (quantizer calls, amax pass included) or flops."""
+        t, h, f = self.t, self.h, self.f
+        q1 = 0.5 + 1.0 / 16  # codes + 1x16 scale bytes per element
+        return {
+            "quantize_x_1x16": ("GB/s", t * h * (2 + 2 + q1)),
+            "quantize_w_16x16": ("GB/s", f * h * (2 + 2 + 2 * (0.5 + 1.0 / 256))),
+            "rht_quantize_dy_sr": ("GB/s", t * f * (2 + 2 + q1)),
+            "rht_quantize_x_rn": ("GB/s", t * h * (2 + 2 + q1)),
+            "gemm_fprop": ("TFLOP/s", 2.0 * t * f * h),
+            "gemm_wgrad": ("TFLOP/s", 2.0 * f * h * t),
+        }
+
+
+def cpu_baseline():
+    """The oracle on a bounded slice of the step: 512 tokens, the first 2048
+    rows of W; same operations and seeds. Returns its effective TFLOP/s."""
+    import numpy as np
+
+    import oracle as o
+    import workloads as wl
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    t, h, f = 2048, HIDDEN, 10240
+    x = wl.normal((t, h), seed=5, outlier_channels=16)
+    w = wl.weight(f, h, seed=2)
+    dy = wl.laplace((t, f), seed=6)
+    t0 = time.perf_counter()
+    qx = o.quantize(x, outputs=("row",))["row"]
+    qw = o.quantize_2d(w)
+    qdy = o.rht_quantize(dy, 7, rounding="sr", seed=7)
+    qxt = o.rht_quantize(x, 7, rounding="rn")
+    o.gemm(qx.codes, qx.scales, qx.tensor_scale, "1d", qw["row"].codes, qw["row"].scales,
+           qw["row"].tensor_scale, "2d")
+    o.gemm(qdy.codes, qdy.scales, qdy.tensor_scale, "1d", qxt.codes, qxt.scales, qxt.tensor_scale,
+           "1d")
+    dt = time.perf_counter() - t0
+    flops = 2 * (2.0 * t * f * h)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"one linear-layer step of the oracle at tokens={t}, hidden={h}, ffn={f} "
+                  f"(first {f} rows of the weight); elementwise numpy single-threaded, float64 "
+                  f"BLAS matmul with {blas_threads} threads; {dt:.1f} s; value = the two GEMMs' "
+                  f"flops / step time",
+        "seconds": dt,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the data-parallel "
+              "path shards by tokens, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import bit_block_scaled_bf16_amd as nv
+    import workloads as wl
+
+    nv.load()
+    torch.cuda.set_device(0)
+    t = args.tokens
+    x_np, w_np, dy_np = wl.linear_layer(tokens=t)
+    step = Step(torch, nv, x_np, w_np, dy_np)
+    del x_np, w_np, dy_np
+    calls = step.calls()
+
+    for _ in range(args.warmup):
+        for _, fn in calls:
+            fn()
+        step.offset += 1
+    torch.cuda.synchronize()
+
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in calls] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for i, (_, fn) in enumerate(calls):
+            events[k][i][0].record()
+            fn()
+            events[k][i][1].record()
+        step.offset += 1
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert int(step.status.cpu()[0]) == 0, "non-finite amax"
+
+    ms_step = elapsed * 1e3 / args.steps
+    work = step.work()
+    kernels = {}
+    for i, (name, _) in enumerate(calls):
+        ms = [events[k][i][0].elapsed_time(events[k][i][1]) for k in range(args.steps)]
+        avg_ms = float(np.mean(ms))
+        unit, amount = work[name]
+        if unit == "GB/s":
+            rate = amount / (avg_ms * 1e-3) / 1e9
+            peak = HBM_PEAK_GBS
+        else:
+            rate = amount / (avg_ms * 1e-3) / 1e12
+            peak = MFMA_PEAK_TFLOPS
+        kernels[name] = {"us": round(avg_ms * 1e3, 2), "achieved": round(rate, 1), "unit": unit,
+                         "frac": round(rate / peak, 4), "work": amount}
+
+    gemm_flops = work["gemm_fprop"][1] + work["gemm_wgrad"][1]
+    value = gemm_flops / (ms_step * 1e-3) / 1e12
+    q_names = [n for n in kernels if kernels[n]["unit"] == "GB/s"]
+    q_bytes = sum(work[n][1] for n in q_names)
+    q_us = sum(kernels[n]["us"] for n in q_names)
+    g_us = kernels["gemm_fprop"]["us"] + kernels["gemm_wgrad"]["us"]
+    dom = max(("gemm_fprop", "gemm_wgrad"), key=lambda n: kernels[n]["us"])
+    roofline = {
+        "bound": "mfma",
+        "kernel": dom,
+        "achieved": kernels[dom]["achieved"],
+        "peak": MFMA_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": kernels[dom]["frac"],
+        "traffic": None,
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 operands (e2m1 x e4m3, exact in f16), f16 MFMA, f32 accumulate; f32 quantizer",
+        "data": "synthetic",
+        "config": {
+            "workload": f"nvfp4_linear_layer_fprop_wgrad tokens={t} hidden={HIDDEN} ffn={FFN}",
+            "x": "bf16 N(0,1), 16 outlier channels x20, seed 5",
+            "w": "bf16 N(0,0.02^2), seed 2, 16x16 blocks",
+            "dy": "bf16 Laplace(0,1e-3), seed 6, RHT seed 7, SR Philox seed 7",
+        },
+        "quantize": {"GB/s": round(q_bytes / (q_us * 1e-6) / 1e9, 1),
+                     "frac": round(q_bytes / (q_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "us": round(q_us, 1)},
+        "gemm": {"TFLOP/s": round(gemm_flops / (g_us * 1e-6) / 1e12, 1),
+                 "frac": round(gemm_flops / (g_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                 "us": round(g_us, 1)},
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -30,22 +30,22 @@ __device__ __forceinline__ float tensor_scale_from_amax(float amax) {
 // E4M3FN byte nearest to t (t >= 0, finite), ties to even mantissa,
 // saturating at 448 (0x7E).
 __device__ __forceinline__ uint32_t e4m3_from_float(float t) {
-  if (t >= 448.0f) return 0x7Eu;
   const uint32_t u = __float_as_uint(t);
-  if (u < 0x3C800000u) {  // t < 2^-6: subnormal grid m * 2^-9 (m == 8 is 2^-6)
-    return static_cast<uint32_t>(__builtin_rintf(t * 512.0f));
-  }
-  // keep 3 mantissa bits, round to nearest even, then rebias 127 -> 7
-  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
-  return (r >> 20) - (120u << 3);
+  // t < 2^-6: subnormal grid m * 2^-9 (m == 8 is 2^-6, byte 0x08)
+  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(fminf(t, 0.015625f) * 512.0f));
+  // otherwise keep 3 mantissa bits, round to nearest even, rebias 127 -> 7
+  const uint32_t nrm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  const uint32_t v = (u < 0x3C800000u) ? sub : nrm;
+  return (t >= 448.0f) ? 0x7Eu : v;
 }
 
-// Value of an E4M3FN byte (never called with the NaN bytes).
+// Value of an E4M3FN byte b in 0x00..0x7E, branch-free: b << 20 places the
+// 4 exponent and 3 mantissa bits at the top of a float32 exponent / mantissa,
+// which is the value times 2^-120 for normal bytes and, as a float32
+// subnormal, m * 2^-129 = (m * 2^-9) * 2^-120 for subnormal ones; the
+// multiply by 2^120 is exact (float32 subnormals are kept).
 __device__ __forceinline__ float e4m3_to_float(uint32_t b) {
-  const uint32_t e = (b >> 3) & 0xFu;
-  const uint32_t m = b & 7u;
-  if (e == 0) return static_cast<float>(m) * 0.001953125f;  // m * 2^-9
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return __uint_as_float((b & 0x7Fu) << 20) * 0x1p120f;
 }
 
 // Block scale and encode multiplier for a block with amax a_b.

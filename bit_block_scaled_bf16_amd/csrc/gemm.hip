@@ -16,13 +16,19 @@
 //
 // Structure. A workgroup of 256 threads computes a 256 x 256 tile of C; its 4
 // waves each own 128 x 128 (4 x 4 MFMA 32x32x16 tiles, float32 accumulators).
-// Per 64-wide K step, each thread loads one row's 32 code bytes of A and of
-// B (plus their scale bytes) from global memory, expands them to fp16 with
-// the gfx950 FP4 -> fp16 converter (exact) and one packed fp16 multiply by
-// the block scale (exact), and writes them to one of two LDS buffers; the
-// MFMAs of the current step read the other buffer. So every element is
-// dequantized once per workgroup, and global loads of step k+1 overlap the
-// MFMAs of step k.
+// The K loop runs in steps of 128. The packed FP4 codes (0.5 byte / element)
+// and the scale bytes of a step go from global memory through registers into
+// a 3-stage LDS ring; each wave then reads the codes of its own rows and
+// columns and expands them to fp16 in registers right before the MFMAs (the
+// gfx950 FP4 -> fp16 converter, then one packed fp16 multiply by the block
+// scale, both exact). Keeping the codes, not fp16 values, in LDS moves a
+// quarter of the bytes through it, which is what bounds this loop on gfx950.
+//
+// K order inside a step. MFMA 32x32x16 takes k-slots 0-7 from lanes 0-31 and
+// 8-15 from lanes 32-63. Any assignment of k to (sub-step, slot) works as
+// long as A and B use the same one, so lane half h takes the 64 consecutive
+// k of [64h, 64h + 64) and sub-step kk uses k = 64h + 8kk + [0, 8): each lane
+// reads 32 contiguous code bytes of a row with two 16-byte LDS reads.
 #include "device_common.h"
 #include "launch.h"
 
@@ -35,12 +41,16 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kBK = 64;                 // K elements per step (4 scale blocks)
+constexpr int kBK = 128;                            // K elements per step
 constexpr int kThreads = 256;
-constexpr int kWaveM = 128;             // rows of C per wave
-constexpr int kWaveN = 128;             // columns of C per wave
-constexpr int kLdsStride = kBK + 8;     // fp16 elements per LDS row (+16 B pad)
-constexpr int kTileHalves = kBM * kLdsStride;
+constexpr int kWaveM = 128;                         // rows of C per wave
+constexpr int kWaveN = 128;                         // columns of C per wave
+constexpr int kStages = 3;                          // LDS ring depth
+constexpr int kCodeStride = kBK / 2 + 16;           // bytes per LDS code row (+16 pad)
+constexpr int kScaleStride = kBK / 16;              // bytes per LDS scale row
+constexpr int kCodeBytes = kBM * kCodeStride;       // one operand's codes per stage
+constexpr int kScaleBytes = kBM * kScaleStride;     // one operand's scales per stage
+constexpr int kStageBytes = 2 * kCodeBytes + 2 * kScaleBytes;
 
 struct GemmParams {
   const uint8_t* qa;
@@ -53,87 +63,111 @@ struct GemmParams {
   int64_t M, N, K, ldc;
 };
 
-// Codes (32 bytes = 64 values) and the 4 scale bytes of one row of one K
-// step, as loaded from global memory.
-struct RowStage {
-  uint4 codes[2];
-  uint32_t scales;  // byte j: scale of values [16j, 16j + 16)
+// One thread's share of one operand for one K step, on its way from global
+// memory to LDS: 4 chunks of 16 code bytes (rows row0 + 64 i, i = 0..3, part
+// `part` of 4) and the 8 scale bytes of row `srow`.
+struct Stage {
+  uint4 codes[4];
+  uint2 scales;
 };
 
-template <bool k2D, bool kAligned>
-__device__ __forceinline__ RowStage load_row(const uint8_t* __restrict__ q,
-                                             const uint8_t* __restrict__ s, int64_t row,
-                                             int64_t rows, int64_t K, int64_t k0) {
-  RowStage st;
-  st.codes[0] = make_uint4(0, 0, 0, 0);
-  st.codes[1] = make_uint4(0, 0, 0, 0);
-  st.scales = 0;
-  if (row >= rows) return st;
-  const int64_t kb = K >> 4;                     // scale bytes per row
-  const int64_t srow = k2D ? (row >> 4) : row;   // scale row
-  const uint8_t* qp = q + row * (K >> 1) + (k0 >> 1);
-  const uint8_t* sp = s + srow * kb + (k0 >> 4);
-  if constexpr (kAligned) {
-    // K % 64 == 0: code rows start on 32-byte and scale rows on 4-byte
-    // boundaries, and there is no K tail
-    st.codes[0] = *reinterpret_cast<const uint4*>(qp);
-    st.codes[1] = *reinterpret_cast<const uint4*>(qp + 16);
-    st.scales = *reinterpret_cast<const uint32_t*>(sp);
-  } else {
-    // rows are only 8-byte aligned; the last step may hold 16, 32 or 48 values
-    const int64_t left = K - k0;
-    const int nblk = left >= kBK ? 4 : static_cast<int>(left >> 4);
-    const uint2* q8 = reinterpret_cast<const uint2*>(qp);
-    uint2 part[4] = {make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0)};
-    uint32_t sc = 0;
+// Per-thread addressing of one operand. Rows past the end are clamped to the
+// last row (every load stays in bounds) and get scale 0, which expands their
+// codes to 0.
+struct OperandSource {
+  const uint8_t* q[4];  // code rows of the 4 chunks (clamped)
+  const uint8_t* s;     // scale row (clamped)
+  bool code_valid[4];
+  bool scale_valid;
+};
+
+template <bool k2D>
+__device__ __forceinline__ OperandSource operand_source(const uint8_t* __restrict__ q,
+                                                        const uint8_t* __restrict__ s,
+                                                        int64_t row0, int64_t rows, int64_t K,
+                                                        int tid) {
+  OperandSource src;
+  const int part = tid & 3;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (b < nblk) {
-        part[b] = q8[b];
-        sc |= static_cast<uint32_t>(sp[b]) << (8 * b);
-      }
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row0 + (tid >> 2) + 64 * i;
+    src.code_valid[i] = row < rows;
+    const int64_t r = row < rows ? row : rows - 1;
+    src.q[i] = q + r * (K >> 1) + 16 * part;
+  }
+  const int64_t srow = row0 + tid;
+  src.scale_valid = srow < rows;
+  const int64_t r = srow < rows ? srow : rows - 1;
+  src.s = s + (k2D ? (r >> 4) : r) * (K >> 4);
+  return src;
+}
+
+// Loads K step `step` (0 <= step < number of steps). With kAligned
+// (K % 128 == 0) every chunk is whole and 16-byte aligned; otherwise each
+// 16-element block is loaded on its own and blocks past K read as zero.
+template <bool kAligned>
+__device__ __forceinline__ Stage load_stage(const OperandSource& src, int step, int64_t K,
+                                            int part) {
+  Stage st;
+  const int64_t k0 = static_cast<int64_t>(step) * kBK;
+  if constexpr (kAligned) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.codes[i] = *reinterpret_cast<const uint4*>(src.q[i] + (k0 >> 1));
+    st.scales = *reinterpret_cast<const uint2*>(src.s + (k0 >> 4));
+  } else {
+    const int64_t kb0 = k0 >> 4;                 // first scale block of the step
+    const int64_t nkb = K >> 4;                  // scale blocks per row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
+      const int64_t b = kb0 + 2 * part;          // this chunk covers blocks b and b + 1
+      if (b < nkb) lo = *reinterpret_cast<const uint2*>(src.q[i] + (k0 >> 1));
+      if (b + 1 < nkb) hi = *reinterpret_cast<const uint2*>(src.q[i] + (k0 >> 1) + 8);
+      st.codes[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
-    st.codes[0] = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
-    st.codes[1] = make_uint4(part[2].x, part[2].y, part[3].x, part[3].y);
-    st.scales = sc;
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t v = (kb0 + j < nkb) ? src.s[kb0 + j] : 0u;
+      if (j < 4) w0 |= v << (8 * j);
+      else w1 |= v << (8 * (j - 4));
+    }
+    st.scales = make_uint2(w0, w1);
   }
   return st;
 }
 
-// fp16 value of an E4M3 scale byte (exact).
-__device__ __forceinline__ _Float16 scale_f16(uint32_t byte) {
-  return static_cast<_Float16>(e4m3_to_float(byte & 0xFFu));
-}
-
-// Expands 8 code bytes (16 values) times a block scale into two half8.
-__device__ __forceinline__ void expand16(uint32_t w0, uint32_t w1, _Float16 sf, half8_t& lo,
-                                         half8_t& hi) {
-  const half2_t s2 = {sf, sf};
-  half2_t h[8];
-  h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0) * s2;
-  h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1) * s2;
-  h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 2) * s2;
-  h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 3) * s2;
-  h[4] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 0) * s2;
-  h[5] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 1) * s2;
-  h[6] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 2) * s2;
-  h[7] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 3) * s2;
-  lo = half8_t{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
-  hi = half8_t{h[4][0], h[4][1], h[5][0], h[5][1], h[6][0], h[6][1], h[7][0], h[7][1]};
-}
-
-// Writes one row stage (64 values) into an LDS tile row.
-__device__ __forceinline__ void store_row(_Float16* __restrict__ lds_row, const RowStage& st) {
-  const uint32_t w[8] = {st.codes[0].x, st.codes[0].y, st.codes[0].z, st.codes[0].w,
-                         st.codes[1].x, st.codes[1].y, st.codes[1].z, st.codes[1].w};
-  half8_t* dst = reinterpret_cast<half8_t*>(lds_row);
+// Writes a stage into LDS (scales of rows past the end become 0 here, when
+// the loaded value is consumed anyway).
+__device__ __forceinline__ void store_stage(uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                            const Stage& st, const OperandSource& src, int tid) {
+  const int part = tid & 3;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    half8_t lo, hi;
-    expand16(w[2 * b], w[2 * b + 1], scale_f16(st.scales >> (8 * b)), lo, hi);
-    dst[2 * b] = lo;
-    dst[2 * b + 1] = hi;
+  for (int i = 0; i < 4; ++i) {
+    *reinterpret_cast<uint4*>(codes + ((tid >> 2) + 64 * i) * kCodeStride + 16 * part) = st.codes[i];
   }
+  const uint2 sc = src.scale_valid ? st.scales : make_uint2(0, 0);
+  *reinterpret_cast<uint2*>(scales + tid * kScaleStride) = sc;
+}
+
+// An E4M3 scale byte b as fp16 bits b << 7 is exactly value(b) / 256: the
+// exponent and mantissa fields line up with fp16's, and subnormal bytes
+// become fp16 subnormals m * 2^-17 = (m * 2^-9) / 256.
+__device__ __forceinline__ _Float16 scale_f16_div256(uint32_t byte) {
+  return __builtin_bit_cast(_Float16, static_cast<uint16_t>((byte & 0x7Fu) << 7));
+}
+
+// Eight codes (one dword) times a block scale as one MFMA fragment. The
+// converter multiplies each E2M1 value by 2^8 (its scale operand acts as a
+// power of two), so (e2m1 * 256) * (s_f / 256) = e2m1 * s_f: every factor
+// and the product are exact in fp16.
+__device__ __forceinline__ half8_t expand8(uint32_t w, _Float16 sf) {
+  const half2_t s2 = {sf, sf};
+  const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s2;
+  const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s2;
+  const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s2;
+  const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * s2;
+  return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
@@ -142,11 +176,72 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
+// Scheduling hints (instruction classes of the gfx9 group scheduler).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedValu = 0x002;
+
+// The codes of this wave's 4 row blocks of A and 4 column blocks of B for
+// one step: two uint4 per block, [0] for sub-steps 0-3 and [1] for 4-7.
+struct Codes {
+  uint4 a[4][2];
+  uint4 b[4][2];
+};
+
+// Scale bytes (4 per block: sub-steps 2j and 2j + 1 use byte j).
+struct Scales {
+  uint32_t a[4];
+  uint32_t b[4];
+};
+
+// Where this lane's fragments sit inside a stage.
+struct FragOffsets {
+  int a_code, b_code, a_scale, b_scale;
+};
+
+template <int kHalf>
+__device__ __forceinline__ void read_codes(Codes& c, const uint8_t* __restrict__ stage,
+                                           const FragOffsets& o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c.a[i][kHalf] = *reinterpret_cast<const uint4*>(stage + o.a_code + i * 32 * kCodeStride + 16 * kHalf);
+    c.b[i][kHalf] = *reinterpret_cast<const uint4*>(stage + kCodeBytes + o.b_code + i * 32 * kCodeStride +
+                                                    16 * kHalf);
+  }
+}
+
+__device__ __forceinline__ void read_scales(Scales& sc, const uint8_t* __restrict__ stage,
+                                            const FragOffsets& o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sc.a[i] = *reinterpret_cast<const uint32_t*>(stage + 2 * kCodeBytes + o.a_scale + i * 32 * kScaleStride);
+    sc.b[i] = *reinterpret_cast<const uint32_t*>(stage + 2 * kCodeBytes + kScaleBytes + o.b_scale +
+                                                 i * 32 * kScaleStride);
+  }
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4 (&c)[2], int kk) {
+  const uint4& v = c[kk >> 2];
+  switch (kk & 3) {
+    case 0: return v.x;
+    case 1: return v.y;
+    case 2: return v.z;
+    default: return v.w;
+  }
+}
+
+// Expands the fragments of sub-step kk.
+__device__ __forceinline__ void expand_substep(half8_t (&af)[4], half8_t (&bf)[4], const Codes& c,
+                                               const Scales& sc, int kk) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    af[i] = expand8(dword_of(c.a[i], kk), scale_f16_div256(sc.a[i] >> (8 * (kk >> 1))));
+    bf[i] = expand8(dword_of(c.b[i], kk), scale_f16_div256(sc.b[i] >> (8 * (kk >> 1))));
+  }
+}
+
 template <bool kA2D, bool kB2D, bool kAligned, bool kBf16Out>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds[4 * kTileHalves];
-  _Float16* lds_a = lds;                      // [2][kBM][kLdsStride]
-  _Float16* lds_b = lds + 2 * kTileHalves;    // [2][kBN][kLdsStride]
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -156,7 +251,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   const int64_t bn = static_cast<int64_t>(blockIdx.x) - bm * tiles_n;
   const int64_t m0 = bm * kBM, n0 = bn * kBN;
   const int64_t K = p.K;
-  const int nsteps = static_cast<int>((K + kBK - 1) / kBK);
+  const int nsteps = static_cast<int>((K + kBK - 1) / kBK);  // >= 1
+  const int last = nsteps - 1;
+  const int part = tid & 3;
 
   floatx16_t acc[4][4];
 #pragma unroll
@@ -166,47 +263,93 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Thread tid stages row tid of the A tile and row tid of the B tile.
-  RowStage sa_st = load_row<kA2D, kAligned>(p.qa, p.sa, m0 + tid, p.M, K, 0);
-  RowStage sb_st = load_row<kB2D, kAligned>(p.qb, p.sb, n0 + tid, p.N, K, 0);
-  if (nsteps > 0) {
-    store_row(lds_a + tid * kLdsStride, sa_st);
-    store_row(lds_b + tid * kLdsStride, sb_st);
+  const OperandSource src_a = operand_source<kA2D>(p.qa, p.sa, m0, p.M, K, tid);
+  const OperandSource src_b = operand_source<kB2D>(p.qb, p.sb, n0, p.N, K, tid);
+
+  // Prologue: steps 0 and 1 into stages 0 and 1; step 2 in flight.
+  {
+    const Stage a0 = load_stage<kAligned>(src_a, 0, K, part);
+    const Stage b0 = load_stage<kAligned>(src_b, 0, K, part);
+    store_stage(lds, lds + 2 * kCodeBytes, a0, src_a, tid);
+    store_stage(lds + kCodeBytes, lds + 2 * kCodeBytes + kScaleBytes, b0, src_b, tid);
+    const int s1 = 1 < last ? 1 : last;
+    const Stage a1 = load_stage<kAligned>(src_a, s1, K, part);
+    const Stage b1 = load_stage<kAligned>(src_b, s1, K, part);
+    uint8_t* st1 = lds + kStageBytes;
+    store_stage(st1, st1 + 2 * kCodeBytes, a1, src_a, tid);
+    store_stage(st1 + kCodeBytes, st1 + 2 * kCodeBytes + kScaleBytes, b1, src_b, tid);
   }
+  Stage a_fly = load_stage<kAligned>(src_a, 2 < last ? 2 : last, K, part);
+  Stage b_fly = load_stage<kAligned>(src_b, 2 < last ? 2 : last, K, part);
   __syncthreads();
 
   const int frag_row = lane & 31;
-  const int frag_k = (lane >> 5) * 8;
+  const int half = lane >> 5;
+  FragOffsets o;
+  o.a_code = (wm * kWaveM + frag_row) * kCodeStride + 32 * half;
+  o.b_code = (wn * kWaveN + frag_row) * kCodeStride + 32 * half;
+  o.a_scale = (wm * kWaveM + frag_row) * kScaleStride + 4 * half;
+  o.b_scale = (wn * kWaveN + frag_row) * kScaleStride + 4 * half;
+
+  // Software pipeline across steps. In sub-step kk of step s the MFMAs of kk
+  // run while the fragments of kk + 1 are expanded (for kk = 7: sub-step 0
+  // of step s + 1). The codes of step s + 1 are read from LDS as soon as the
+  // ones they replace are dead: the sub-step 0-3 halves after sub-step 2,
+  // the 4-7 halves in sub-step 7. Stage s + 1 was written in step s - 1,
+  // before the barrier that ended it.
+  Codes c;
+  Scales sc, sc_next;
+  read_codes<0>(c, lds, o);
+  read_codes<1>(c, lds, o);
+  read_scales(sc, lds, o);
+  half8_t af[2][4], bf[2][4];
+  expand_substep(af[0], bf[0], c, sc, 0);
+
+  int cur = 0;  // stage holding step s
   for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) {
-      const int64_t k1 = static_cast<int64_t>(step + 1) * kBK;
-      sa_st = load_row<kA2D, kAligned>(p.qa, p.sa, m0 + tid, p.M, K, k1);
-      sb_st = load_row<kB2D, kAligned>(p.qb, p.sb, n0 + tid, p.N, K, k1);
-    }
-    const _Float16* a_tile = lds_a + cur * kTileHalves + (wm * kWaveM + frag_row) * kLdsStride + frag_k;
-    const _Float16* b_tile = lds_b + cur * kTileHalves + (wn * kWaveN + frag_row) * kLdsStride + frag_k;
+    const int nxt = cur == 2 ? 0 : cur + 1;       // stage of step s + 1
+    const int wr = cur == 0 ? 2 : cur - 1;        // stage for step s + 2
+    const uint8_t* next_stage = lds + nxt * kStageBytes;
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
-      half8_t af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const half8_t*>(a_tile + i * 32 * kLdsStride + kk);
-        bf[i] = *reinterpret_cast<const half8_t*>(b_tile + i * 32 * kLdsStride + kk);
-      }
+    for (int kk = 0; kk < 8; ++kk) {
+      const int b = kk & 1;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      const int nxt = cur ^ 1;
-      store_row(lds_a + nxt * kTileHalves + tid * kLdsStride, sa_st);
-      store_row(lds_b + nxt * kTileHalves + tid * kLdsStride, sb_st);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[b][i], bf[b][j], acc[i][j], 0, 0, 0);
+      if (kk < 7) {
+        expand_substep(af[b ^ 1], bf[b ^ 1], c, sc, kk + 1);
+      } else {
+        expand_substep(af[0], bf[0], c, sc_next, 0);  // step s + 1, sub-step 0
+      }
+      if (kk == 1) {
+        // step s + 2 (loaded during step s - 1) into the stage that held
+        // step s - 1, then request step s + 3
+        uint8_t* st = lds + wr * kStageBytes;
+        store_stage(st, st + 2 * kCodeBytes, a_fly, src_a, tid);
+        store_stage(st + kCodeBytes, st + 2 * kCodeBytes + kScaleBytes, b_fly, src_b, tid);
+        const int ld = (step + 3) < last ? (step + 3) : last;
+        a_fly = load_stage<kAligned>(src_a, ld, K, part);
+        b_fly = load_stage<kAligned>(src_b, ld, K, part);
+      }
+      if (kk == 3) {
+        read_codes<0>(c, next_stage, o);
+        read_scales(sc_next, next_stage, o);
+      }
+      if (kk == 6) read_codes<1>(c, next_stage, o);
+#ifndef NVFP4_NO_SCHED_HINTS
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#endif
     }
     __syncthreads();
+    sc = sc_next;
+    cur = nxt;
   }
 
   // Epilogue: C = acc * (S_A * S_B); lane holds column lane % 32 and rows
@@ -285,7 +428,7 @@ int launch_gemm(const GemmLaunch& g, hipStream_t stream) {
   p.N = g.N;
   p.K = g.K;
   p.ldc = g.ldc;
-  const bool aligned = (g.K % 64) == 0;
+  const bool aligned = (g.K % kBK) == 0;
   if (g.a_2d) {
     return g.b_2d ? launch_blocks<true, true>(p, aligned, g.c_bf16, stream)
                   : launch_blocks<true, false>(p, aligned, g.c_bf16, stream);

@@ -288,34 +288,38 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
       }
     } else {
       if (out_row) {
-        // 1x16 blocks along the row: this lane's 8 values + lane ^ 1's 8
+        // 1x16 blocks along the row: this lane's 8 values + lane ^ 1's 8.
+        // Rows past a ragged end are skipped by a predicate (the same for
+        // both lanes of a pair), not a loop exit, so the register tile keeps
+        // static indices.
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          if (i >= t.nrows) break;  // same for both lanes of a block pair
-          uint32_t am = 0;
+          if (i < t.nrows) {
+            uint32_t am = 0;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t b = abs_bits(v[i][j]);
-            am = (b > am) ? b : am;
-          }
-          const uint32_t other = swap_adjacent_lanes(am);
-          am = (other > am) ? other : am;
-          const BlockScale bs = block_scale(__uint_as_float(am), six_s, s);
-          float y[8];
+            for (int j = 0; j < 8; ++j) {
+              const uint32_t b = abs_bits(v[i][j]);
+              am = (b > am) ? b : am;
+            }
+            const uint32_t other = swap_adjacent_lanes(am);
+            am = (other > am) ? other : am;
+            const BlockScale bs = block_scale(__uint_as_float(am), six_s, s);
+            float y[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) y[j] = __fmul_rn(v[i][j], bs.mult);
-          uint32_t w;
-          if constexpr (kSR) {
-            const uint64_t e = static_cast<uint64_t>(t.r0 + i) * static_cast<uint64_t>(cols) +
-                               static_cast<uint64_t>(t.c0);
-            w = pack8_sr(y, sr_words(p.k0, p.k1, e >> 3, p.offset, kStreamRow));
-          } else {
-            w = pack8_rn(y);
-          }
-          if (bs.byte == 0u) w = 0u;
-          *reinterpret_cast<uint32_t*>(p.q_row + (t.r0 + i) * (cols >> 1) + (t.c0 >> 1)) = w;
-          if ((t.cg & 1) == 0) {
-            p.s_row[(t.r0 + i) * (cols >> 4) + (t.c0 >> 4)] = static_cast<uint8_t>(bs.byte);
+            for (int j = 0; j < 8; ++j) y[j] = __fmul_rn(v[i][j], bs.mult);
+            uint32_t w;
+            if constexpr (kSR) {
+              const uint64_t e = static_cast<uint64_t>(t.r0 + i) * static_cast<uint64_t>(cols) +
+                                 static_cast<uint64_t>(t.c0);
+              w = pack8_sr(y, sr_words(p.k0, p.k1, e >> 3, p.offset, kStreamRow));
+            } else {
+              w = pack8_rn(y);
+            }
+            if (bs.byte == 0u) w = 0u;
+            *reinterpret_cast<uint32_t*>(p.q_row + (t.r0 + i) * (cols >> 1) + (t.c0 >> 1)) = w;
+            if ((t.cg & 1) == 0) {
+              p.s_row[(t.r0 + i) * (cols >> 4) + (t.c0 >> 4)] = static_cast<uint8_t>(bs.byte);
+            }
           }
         }
       }
