@@ -170,10 +170,12 @@ __device__ __forceinline__ half8_t expand8(uint32_t w, _Float16 sf) {
   return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  const uint32_t b = __float_as_uint(f);
-  if ((b & 0x7F800000u) == 0x7F800000u) return (b >> 16) | ((b & 0xFFFFu) ? 0x40u : 0u);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+// Two float32 -> two bf16 (round to nearest even; gfx950 converts a pair in
+// one instruction), low half = a.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const bf16x2_t h = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 // Scheduling hints (instruction classes of the gfx9 group scheduler).
@@ -266,21 +268,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   const OperandSource src_a = operand_source<kA2D>(p.qa, p.sa, m0, p.M, K, tid);
   const OperandSource src_b = operand_source<kB2D>(p.qb, p.sb, n0, p.N, K, tid);
 
-  // Prologue: steps 0 and 1 into stages 0 and 1; step 2 in flight.
-  {
-    const Stage a0 = load_stage<kAligned>(src_a, 0, K, part);
-    const Stage b0 = load_stage<kAligned>(src_b, 0, K, part);
-    store_stage(lds, lds + 2 * kCodeBytes, a0, src_a, tid);
-    store_stage(lds + kCodeBytes, lds + 2 * kCodeBytes + kScaleBytes, b0, src_b, tid);
-    const int s1 = 1 < last ? 1 : last;
-    const Stage a1 = load_stage<kAligned>(src_a, s1, K, part);
-    const Stage b1 = load_stage<kAligned>(src_b, s1, K, part);
-    uint8_t* st1 = lds + kStageBytes;
-    store_stage(st1, st1 + 2 * kCodeBytes, a1, src_a, tid);
-    store_stage(st1 + kCodeBytes, st1 + 2 * kCodeBytes + kScaleBytes, b1, src_b, tid);
-  }
-  Stage a_fly = load_stage<kAligned>(src_a, 2 < last ? 2 : last, K, part);
-  Stage b_fly = load_stage<kAligned>(src_b, 2 < last ? 2 : last, K, part);
+  // Prologue: steps 0, 1 and 2 requested together; 0 and 1 go to stages 0
+  // and 1, step 2 stays in flight.
+  const int s1 = 1 < last ? 1 : last;
+  const int s2 = 2 < last ? 2 : last;
+  const Stage a0 = load_stage<kAligned>(src_a, 0, K, part);
+  const Stage b0 = load_stage<kAligned>(src_b, 0, K, part);
+  const Stage a1 = load_stage<kAligned>(src_a, s1, K, part);
+  const Stage b1 = load_stage<kAligned>(src_b, s1, K, part);
+  Stage a_fly = load_stage<kAligned>(src_a, s2, K, part);
+  Stage b_fly = load_stage<kAligned>(src_b, s2, K, part);
+  store_stage(lds, lds + 2 * kCodeBytes, a0, src_a, tid);
+  store_stage(lds + kCodeBytes, lds + 2 * kCodeBytes + kScaleBytes, b0, src_b, tid);
+  store_stage(lds + kStageBytes, lds + kStageBytes + 2 * kCodeBytes, a1, src_a, tid);
+  store_stage(lds + kStageBytes + kCodeBytes, lds + kStageBytes + 2 * kCodeBytes + kScaleBytes, b1,
+              src_b, tid);
   __syncthreads();
 
   const int frag_row = lane & 31;
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[b][i], bf[b][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[b][j], af[b][i], acc[i][j], 0, 0, 0);
       if (kk < 7) {
         expand_substep(af[b ^ 1], bf[b ^ 1], c, sc, kk + 1);
       } else {
@@ -352,26 +354,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     cur = nxt;
   }
 
-  // Epilogue: C = acc * (S_A * S_B); lane holds column lane % 32 and rows
-  // 8 * (e / 4) + 4 * (lane / 32) + e % 4 of each 32 x 32 tile.
+  // Epilogue: C = acc * (S_A * S_B). The MFMAs took B as their first operand,
+  // so each accumulator tile is C^T in the MFMA output layout: lane l holds
+  // row l % 32 of the 32 x 32 tile and, in elements 4g .. 4g + 3, its four
+  // consecutive columns 8g + 4(l / 32) .. + 3. They leave as one 8-byte (bf16)
+  // or 16-byte (float32) store; ragged edges and unaligned rows fall back to
+  // element stores.
   const float scale = __fmul_rn(*p.ta, *p.tb);
-  const int col_l = lane & 31;
-  const int row_l = (lane >> 5) * 4;
+  const int row_l = lane & 31;
+  const int col_l = (lane >> 5) * 4;
+  const bool vec_ok = ((p.ldc & 3) == 0) &&
+                      ((reinterpret_cast<uintptr_t>(p.c) & (kBf16Out ? 7u : 15u)) == 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const int64_t row = m0 + wm * kWaveM + i * 32 + row_l;
+    if (row >= p.M) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * kWaveN + j * 32 + col_l;
-      if (col >= p.N) continue;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * kWaveM + i * 32 + (e >> 2) * 8 + row_l + (e & 3);
-        if (row < p.M) {
-          const float v = __fmul_rn(acc[i][j][e], scale);
+      for (int g = 0; g < 4; ++g) {
+        const int64_t col = n0 + wn * kWaveN + j * 32 + 8 * g + col_l;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __fmul_rn(acc[i][j][4 * g + e], scale);
+        if (vec_ok && col + 3 < p.N) {
           if constexpr (kBf16Out) {
-            static_cast<uint16_t*>(p.c)[row * p.ldc + col] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+            const uint32_t lo = f32x2_to_bf16x2(v[0], v[1]);
+            const uint32_t hi = f32x2_to_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.c) + row * p.ldc + col) = make_uint2(lo, hi);
           } else {
-            static_cast<float*>(p.c)[row * p.ldc + col] = v;
+            *reinterpret_cast<float4*>(static_cast<float*>(p.c) + row * p.ldc + col) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (col + e < p.N) {
+              if constexpr (kBf16Out) {
+                static_cast<uint16_t*>(p.c)[row * p.ldc + col + e] =
+                    static_cast<uint16_t>(f32x2_to_bf16x2(v[e], 0.0f) & 0xFFFFu);
+              } else {
+                static_cast<float*>(p.c)[row * p.ldc + col + e] = v[e];
+              }
+            }
           }
         }
       }

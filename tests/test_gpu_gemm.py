@@ -85,6 +85,35 @@ def test_gemm_all_ones_closed_form():
     assert np.all(host(c) == float(k))
 
 
+def test_gemm_bf16_output_rounds_to_nearest_even():
+    """C = 1 + 2^-8 and 1 + 3 * 2^-8 are exact float32 sums that sit halfway
+    between bf16 neighbours; round to nearest even gives 1.0 and 1.015625."""
+    torch = require_gpu()
+    import bit_block_scaled_bf16_amd as nv
+
+    k = 32
+    # row 0: block 0 = one 1.0 (code 0x2, scale 0x38); block 1 = one 0.5 (code
+    # 0x1) at scale 2^-7 (0x04) -> 2^-8. row 1: same with 3 * 0.5 * 2^-7.
+    qa = torch.zeros((2, k // 2), dtype=torch.uint8, device="cuda")
+    qa[0, 0] = 0x02
+    qa[0, 8] = 0x01
+    qa[1, 0] = 0x02
+    qa[1, 8] = 0x11  # two 0.5 values
+    qa[1, 9] = 0x01  # a third 0.5
+    sa = torch.tensor([[0x38, 0x04], [0x38, 0x04]], dtype=torch.uint8, device="cuda")
+    qb = torch.full((16, k // 2), 0x22, dtype=torch.uint8, device="cuda")  # all 1.0
+    sb = torch.full((16, k // 16), 0x38, dtype=torch.uint8, device="cuda")
+    one = torch.tensor([1.0, 0, 0, 0], dtype=torch.float32, device="cuda")
+    c = torch.empty((2, 16), dtype=torch.bfloat16, device="cuda")
+    nv.nvfp4_gemm(qa, sa, one, nv.BLOCK_1D, qb, sb, one, nv.BLOCK_1D, 2, 16, k, c)
+    got = host(c.float())
+    assert np.all(got[0] == 1.0) and np.all(got[1] == 1.015625)
+    c32 = torch.empty((2, 16), dtype=torch.float32, device="cuda")
+    nv.nvfp4_gemm(qa, sa, one, nv.BLOCK_1D, qb, sb, one, nv.BLOCK_1D, 2, 16, k, c32)
+    got32 = host(c32)
+    assert np.all(got32[0] == 1.0 + 2.0 ** -8) and np.all(got32[1] == 1.0 + 3 * 2.0 ** -8)
+
+
 def test_gemm_empty_k_writes_zeros():
     torch = require_gpu()
     import bit_block_scaled_bf16_amd as nv
