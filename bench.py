@@ -37,6 +37,11 @@ MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 MFMA, MI355X
 
 TOKENS, HIDDEN, FFN = 16384, 5120, 20480
 
+# HBM traffic per GEMM launch comes from the committed counter summary below
+# (null when it is missing or the GEMM source changed since it was taken).
+TRAFFIC_SUMMARY = "linear_layer_traffic.md"
+GEMM_KERNEL_NAMES = {"gemm_fprop": "gemm_kernel<false, true,", "gemm_wgrad": "gemm_kernel<false, false,"}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -45,6 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=int, default=TOKENS)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, run one copy-like kernel (torch.bitwise_not on int32) "
+                         "over this many MiB, the reference for the traffic counters")
     return ap.parse_args()
 
 
@@ -173,6 +181,13 @@ def main():
     step = Step(torch, nv, x_np, w_np, dy_np)
     del x_np, w_np, dy_np
     calls = step.calls()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         for _, fn in calls:
@@ -217,6 +232,10 @@ def main():
     q_us = sum(kernels[n]["us"] for n in q_names)
     g_us = kernels["gemm_fprop"]["us"] + kernels["gemm_wgrad"]["us"]
     dom = max(("gemm_fprop", "gemm_wgrad"), key=lambda n: kernels[n]["us"])
+    from bit_block_scaled_bf16_amd import profiling
+
+    traffic = profiling.kernel_traffic(
+        os.path.join(ROOT, "profiles", TRAFFIC_SUMMARY), GEMM_KERNEL_NAMES[dom], "gemm_kernel")
     roofline = {
         "bound": "mfma",
         "kernel": dom,
@@ -224,7 +243,7 @@ def main():
         "peak": MFMA_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": kernels[dom]["frac"],
-        "traffic": None,
+        "traffic": traffic,
     }
     out = {
         "metric": METRIC,

@@ -1,0 +1,188 @@
+"""Measurement helpers: summaries of rocprofv3 output for profiles/.
+
+Usage (after the rocprofv3 runs that bench.py's docstring lists):
+
+  python -m bit_block_scaled_bf16_amd.profiling stats  <kernel_stats.csv> <out.md> <command>
+  python -m bit_block_scaled_bf16_amd.profiling traffic <fetch_dir> <write_dir> <copy_bytes> \
+        <out.md> <command>
+
+`stats` condenses a --kernel-trace --stats CSV into a table of average kernel
+durations. `traffic` turns two --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB
+per dispatch) into bytes per launch, each scaled by what the same counter
+reads for a copy-like kernel of known size (torch's elementwise bitwise_not,
+which reads and writes the same number of bytes, run by bench.py
+--copy-calibration-mib). The traffic summary carries the SHA-256 of
+each kernel source it covers; bench.py reports the figure only while the
+source is unchanged.
+"""
+
+from __future__ import annotations
+
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+# Name fragment of the copy-like calibration kernel (bench.py
+# --copy-calibration-mib runs torch.bitwise_not on int32 tensors of that size).
+CALIBRATION_KERNEL = "bitwise_not"
+
+# Kernel name fragment -> source file whose hash the traffic figure covers.
+KERNEL_SOURCES = {
+    "gemm_kernel": "gemm.hip",
+    "quantize_kernel": "quantize.hip",
+    "amax_kernel": "quantize.hip",
+}
+
+
+def source_hash(fname: str) -> str:
+    with open(os.path.join(CSRC, fname), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def short_name(name: str) -> str:
+    """Kernel name without namespaces, return type and parameter list."""
+    name = name.replace("nvfp4::(anonymous namespace)::", "").replace("nvfp4::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    if "<" in name and name.index("<") < name.find("(") if "(" in name else False:
+        return name[: name.index(">") + 1]
+    return name.split("(")[0]
+
+
+def stats_summary(csv_path: str, out_md: str, command: str) -> None:
+    rows = list(csv.DictReader(open(csv_path)))
+    lines = [
+        "# Kernel durations (rocprofv3 --kernel-trace --stats)",
+        "",
+        f"Command: `{command}`",
+        "",
+        "| kernel | calls | average us | min us | max us | share % |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in rows:
+        lines.append(
+            f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+            f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+            f"{float(r['Percentage']):.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(run_dir: str, counter: str):
+    path = None
+    for root, _, files in os.walk(run_dir):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                path = os.path.join(root, fn)
+    if path is None:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    agg = collections.defaultdict(float)
+    names = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        agg[d] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    return [(d, names[d], agg[d]) for d in sorted(agg)]
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, copy_bytes: int, out_md: str,
+                    command: str) -> dict:
+    fetch = _per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _per_dispatch(write_dir, "WRITE_SIZE")
+    # the calibration kernel: torch's elementwise bitwise_not over int32, which
+    # reads and writes copy_bytes each, like a plain copy
+    copy_f = [v for _, n, v in fetch if CALIBRATION_KERNEL in n]
+    copy_w = [v for _, n, v in write if CALIBRATION_KERNEL in n]
+    kib_f = max(copy_f)
+    kib_w = max(copy_w)
+    f_read = copy_bytes / (kib_f * 1024.0)
+    f_write = copy_bytes / (kib_w * 1024.0)
+    per_kernel = collections.defaultdict(lambda: {"fetch": [], "write": []})
+    for _, n, v in fetch:
+        per_kernel[short_name(n)]["fetch"].append(v * 1024.0 * f_read)
+    for _, n, v in write:
+        per_kernel[short_name(n)]["write"].append(v * 1024.0 * f_write)
+    result = {
+        "command": command,
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": kib_f,
+        "copy_write_kib": kib_w,
+        "read_factor": f_read,
+        "write_factor": f_write,
+        "sources": {k: source_hash(v) for k, v in sorted(set(KERNEL_SOURCES.items()))},
+        "kernels": {},
+    }
+    for name, d in per_kernel.items():
+        if not d["fetch"] or not d["write"]:
+            continue
+        n = min(len(d["fetch"]), len(d["write"]))
+        result["kernels"][name] = {
+            "dispatches": n,
+            "fetch_bytes": [round(x) for x in d["fetch"][:n]],
+            "write_bytes": [round(x) for x in d["write"][:n]],
+        }
+    lines = [
+        "# HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)",
+        "",
+        f"Command (run once with `--pmc FETCH_SIZE`, once with `--pmc WRITE_SIZE`): `{command}`",
+        "",
+        f"Calibration: a plain copy of {copy_bytes} bytes reads FETCH_SIZE = {kib_f:.0f} KiB and "
+        f"WRITE_SIZE = {kib_w:.0f} KiB, so the counters are scaled by {f_read:.3f} (reads) and "
+        f"{f_write:.3f} (writes).",
+        "",
+        "| kernel | dispatch | fetched MB | written MB |",
+        "|---|---|---|---|",
+    ]
+    for name, d in result["kernels"].items():
+        for i, (fb, wb) in enumerate(zip(d["fetch_bytes"], d["write_bytes"])):
+            lines.append(f"| `{name}` | {i} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+    lines += ["", "```json", json.dumps(result, indent=1), "```", ""]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    return result
+
+
+def load_traffic(md_path: str):
+    """The JSON block of a traffic summary, or None."""
+    if not os.path.exists(md_path):
+        return None
+    text = open(md_path).read()
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    return json.loads(m.group(1)) if m else None
+
+
+def kernel_traffic(md_path: str, name_fragment: str, source_key: str, dispatch_index: int = 0):
+    """HBM bytes (read + write) of one dispatch of the kernel whose short name
+    contains name_fragment, or None when the summary is missing or the
+    kernel's source changed since it was taken."""
+    data = load_traffic(md_path)
+    if data is None:
+        return None
+    src = KERNEL_SOURCES.get(source_key)
+    if src is None or data["sources"].get(source_key) != source_hash(src):
+        return None
+    for name, d in data["kernels"].items():
+        if name_fragment in name and dispatch_index < d["dispatches"]:
+            return d["fetch_bytes"][dispatch_index] + d["write_bytes"][dispatch_index]
+    return None
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        stats_summary(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "traffic":
+        r = traffic_summary(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5], sys.argv[6])
+        print(json.dumps({k: v for k, v in r.items() if k != "kernels"}, indent=1))
+    else:
+        raise SystemExit(__doc__)
