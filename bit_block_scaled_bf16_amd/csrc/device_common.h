@@ -58,7 +58,10 @@ __device__ __forceinline__ BlockScale block_scale(float amax_b, float six_s, flo
   BlockScale bs;
   bs.byte = e4m3_from_float(__fdiv_rn(amax_b, six_s));
   const float sf = e4m3_to_float(bs.byte);
-  bs.mult = (bs.byte == 0u) ? 0.0f : __fdiv_rn(1.0f, __fmul_rn(sf, s));
+  // the division always runs (on 1.0 for a zero scale), so no branch
+  const float denom = (bs.byte == 0u) ? 1.0f : __fmul_rn(sf, s);
+  const float r = __fdiv_rn(1.0f, denom);
+  bs.mult = (bs.byte == 0u) ? 0.0f : r;
   return bs;
 }
 
@@ -89,25 +92,24 @@ __device__ __forceinline__ uint32_t pack8_rn(const float* y) {
 
 // Stochastically rounded E2M1 code of y from 16 random bits u16: with
 // a = min(|y|, 6), lo the largest magnitude <= a and hi the next one, round
-// up exactly when u16 / 2^16 < (a - lo) / (hi - lo). The comparison is done
-// on integers / exact floats, so it is exact.
+// up exactly when u16 / 2^16 < (a - lo) / (hi - lo).
+//
+// One branch-free formula covers every magnitude: with e' = max(exponent of
+// a, 0) (0 below 2, 1 in [2, 4), 2 in [4, 6]), v = a * 2^(1 - e') lies in
+// [0, 4) and the E2M1 grid around a maps to the integers around v, so
+// lo's code is floor(v) + 2 e' and the fraction is v - floor(v). Scaling by a
+// power of two, floor and the subtraction are exact in float32, so the
+// comparison with u16 / 2^16 is exact too.
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
   const uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
   const float a = fminf(fabsf(y), 6.0f);
-  const uint32_t u = __float_as_uint(a);
-  uint32_t code;
-  if (u >= 0x3F800000u) {
-    // a >= 1: magnitude code is exponent:top mantissa bit; the 22 bits below
-    // are (a - lo) / step * 2^22
-    code = (u >> 22) - 252u;
-    code += ((u16 << 6) < (u & 0x3FFFFFu)) ? 1u : 0u;
-  } else if (u >= 0x3F000000u) {
-    // 0.5 <= a < 1: lo = 0.5, step 0.5, fraction = 23 mantissa bits
-    code = 1u + (((u16 << 7) < (u & 0x7FFFFFu)) ? 1u : 0u);
-  } else {
-    // a < 0.5: lo = 0, step 0.5, fraction = 2a
-    code = (static_cast<float>(u16) < a * 131072.0f) ? 1u : 0u;
-  }
+  const int e = static_cast<int>(__float_as_uint(a) >> 23) - 127;
+  const int ep = e > 0 ? e : 0;
+  const float v = a * __uint_as_float(static_cast<uint32_t>(128 - ep) << 23);  // a * 2^(1 - e')
+  const float fl = __builtin_floorf(v);
+  const float frac = v - fl;
+  const uint32_t code = static_cast<uint32_t>(fl) + 2u * static_cast<uint32_t>(ep) +
+                        ((static_cast<float>(u16) < frac * 65536.0f) ? 1u : 0u);
   return code | sign;
 }
 

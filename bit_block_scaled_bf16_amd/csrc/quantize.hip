@@ -61,17 +61,24 @@ __device__ __forceinline__ Tile locate(int64_t rows, int64_t cols) {
 }
 
 // Loads this lane's 16 x 8 values as float32 (bf16 widened exactly).
-// Rows at or beyond r0 + nrows (a row count that is not a multiple of 16, only
-// allowed for the row-blocked copy) read as zero.
-template <typename InT>
+// Loads this lane's 16 x 8 values as float32 (bf16 widened exactly). With
+// kRagged, rows at or beyond r0 + nrows (a row count that is not a multiple
+// of 16, allowed only for the row-blocked copy) read as zero; otherwise all
+// 16 rows exist and the loads are unconditional.
+template <typename InT, bool kRagged>
 __device__ __forceinline__ void load_sub_tile(const InT* __restrict__ x, int64_t ldx, int64_t r0,
                                               int64_t c0, int nrows, float (&v)[16][8]) {
+  const InT* row = x + r0 * ldx + c0;
   if constexpr (sizeof(InT) == 2) {
     uint4 raw[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      raw[i] = (i < nrows) ? *reinterpret_cast<const uint4*>(x + (r0 + i) * ldx + c0)
-                           : make_uint4(0u, 0u, 0u, 0u);
+      if (!kRagged || i < nrows) {
+        raw[i] = *reinterpret_cast<const uint4*>(row);
+      } else {
+        raw[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      row += ldx;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -86,13 +93,14 @@ __device__ __forceinline__ void load_sub_tile(const InT* __restrict__ x, int64_t
     float4 raw[16][2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i < nrows) {
-        raw[i][0] = *reinterpret_cast<const float4*>(x + (r0 + i) * ldx + c0);
-        raw[i][1] = *reinterpret_cast<const float4*>(x + (r0 + i) * ldx + c0 + 4);
+      if (!kRagged || i < nrows) {
+        raw[i][0] = *reinterpret_cast<const float4*>(row);
+        raw[i][1] = *reinterpret_cast<const float4*>(row + 4);
       } else {
         raw[i][0] = make_float4(0.f, 0.f, 0.f, 0.f);
         raw[i][1] = raw[i][0];
       }
+      row += ldx;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -133,7 +141,7 @@ __device__ __forceinline__ void block_max_to_global(uint32_t m, uint32_t* lds4, 
 // ---------------------------------------------------------------------------
 // Tensor amax (optionally of the Hadamard-transformed tensor).
 // ---------------------------------------------------------------------------
-template <typename InT, bool kRht>
+template <typename InT, bool kRht, bool kRagged>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const InT* __restrict__ x, int64_t rows,
                                                         int64_t cols, int64_t ldx,
                                                         uint32_t sign_mask, float* amax_out) {
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const InT* __restrict__ 
   uint32_t m = 0;
   if (t.valid) {
     float v[16][8];
-    load_sub_tile<InT>(x, ldx, t.r0, t.c0, t.nrows, v);
+    load_sub_tile<InT, kRagged>(x, ldx, t.r0, t.c0, t.nrows, v);
     if constexpr (kRht) rht_columns(v, sign_mask);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -215,11 +223,13 @@ __device__ __forceinline__ void column_block(const float (&col)[16], float six_s
     w0 = pack8_rn(y);
     w1 = pack8_rn(y + 8);
   }
-  if (bs.byte == 0u) w0 = w1 = 0u;
+  const uint32_t keep = (bs.byte == 0u) ? 0u : 0xFFFFFFFFu;
+  w0 &= keep;
+  w1 &= keep;
   sbyte = bs.byte;
 }
 
-template <typename InT, int kMode, bool kSR>
+template <typename InT, int kMode, bool kSR, bool kRagged>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_codes[kTileCols * kLdsCodeStride];
   __shared__ uint8_t lds_scales[kTileCols * kLdsScaleStride];
@@ -240,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
 
   if (t.valid) {
     float v[16][8];
-    load_sub_tile<InT>(static_cast<const InT*>(p.x), p.ldx, t.r0, t.c0, t.nrows, v);
+    load_sub_tile<InT, kRagged>(static_cast<const InT*>(p.x), p.ldx, t.r0, t.c0, t.nrows, v);
     if constexpr (kMode == kModeRHT) rht_columns(v, p.sign_mask);
 
     if constexpr (kMode == kMode2D) {
@@ -260,7 +270,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
       for (int i = 0; i < 16; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[i][j] = __fmul_rn(v[i][j], bs.mult);
-      const bool zero = bs.byte == 0u;
+      // codes of a zero-scale tile are 0 (a mask, not a branch)
+      const uint32_t keep = (bs.byte == 0u) ? 0u : 0xFFFFFFFFu;
       if ((t.cg & 1) == 0) {
         if (out_row) p.s_row[(t.r0 >> 4) * (cols >> 4) + (t.c0 >> 4)] = static_cast<uint8_t>(bs.byte);
         if (out_col) p.s_col[(t.c0 >> 4) * (rows >> 4) + (t.r0 >> 4)] = static_cast<uint8_t>(bs.byte);
@@ -268,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
       if (out_row) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const uint32_t w = zero ? 0u : pack8_rn(v[i]);
+          const uint32_t w = pack8_rn(v[i]) & keep;
           *reinterpret_cast<uint32_t*>(p.q_row + (t.r0 + i) * (cols >> 1) + (t.c0 >> 1)) = w;
         }
       }
@@ -278,8 +289,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
           float col[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i) col[i] = v[i][j];
-          const uint32_t w0 = zero ? 0u : pack8_rn(col);
-          const uint32_t w1 = zero ? 0u : pack8_rn(col + 8);
+          const uint32_t w0 = pack8_rn(col) & keep;
+          const uint32_t w1 = pack8_rn(col + 8) & keep;
           uint32_t* dst = reinterpret_cast<uint32_t*>(lds_codes + (c_local0 + j) * kLdsCodeStride +
                                                       (r_local >> 1));
           dst[0] = w0;
@@ -294,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
         // static indices.
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          if (i < t.nrows) {
+          if (!kRagged || i < t.nrows) {
             uint32_t am = 0;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -315,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
             } else {
               w = pack8_rn(y);
             }
-            if (bs.byte == 0u) w = 0u;
+            w &= (bs.byte == 0u) ? 0u : 0xFFFFFFFFu;
             *reinterpret_cast<uint32_t*>(p.q_row + (t.r0 + i) * (cols >> 1) + (t.c0 >> 1)) = w;
             if ((t.cg & 1) == 0) {
               p.s_row[(t.r0 + i) * (cols >> 4) + (t.c0 >> 4)] = static_cast<uint8_t>(bs.byte);
@@ -370,33 +381,41 @@ int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
                 uint32_t sign_mask, float* amax_ws, hipStream_t stream) {
   fill_f32_kernel<<<1, 64, 0, stream>>>(amax_ws, 0.0f);
   const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
+  const unsigned g = static_cast<unsigned>(tiles);
+  const bool ragged = (rows % 16) != 0;
   if (rht) {
-    amax_kernel<InT, true><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(
-        x, rows, cols, ldx, sign_mask, amax_ws);
+    amax_kernel<InT, true, false><<<g, kThreads, 0, stream>>>(x, rows, cols, ldx, sign_mask, amax_ws);
+  } else if (ragged) {
+    amax_kernel<InT, false, true><<<g, kThreads, 0, stream>>>(x, rows, cols, ldx, sign_mask, amax_ws);
   } else {
-    amax_kernel<InT, false><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(
-        x, rows, cols, ldx, sign_mask, amax_ws);
+    amax_kernel<InT, false, false><<<g, kThreads, 0, stream>>>(x, rows, cols, ldx, sign_mask, amax_ws);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <typename InT, int kMode, bool kSR>
+template <typename InT, int kMode, bool kSR, bool kRagged>
 void launch_quant(const QuantParams& p, hipStream_t stream) {
   const int64_t tiles =
       ((p.rows + kTileRows - 1) / kTileRows) * ((p.cols + kTileCols - 1) / kTileCols);
-  quantize_kernel<InT, kMode, kSR><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(p);
+  quantize_kernel<InT, kMode, kSR, kRagged><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(p);
 }
 
+// Ragged row counts (rows % 16 != 0) only reach the 1x16 row-only path: the
+// column copy, 16x16 blocks and the RHT path require rows % 16 == 0.
 template <typename InT>
 void dispatch_quant(const QuantParams& p, int mode, bool sr, hipStream_t stream) {
+  const bool ragged = (p.rows % 16) != 0;
   if (mode == kMode2D) {
-    launch_quant<InT, kMode2D, false>(p, stream);
+    launch_quant<InT, kMode2D, false, false>(p, stream);
   } else if (mode == kModeRHT) {
-    if (sr) launch_quant<InT, kModeRHT, true>(p, stream);
-    else launch_quant<InT, kModeRHT, false>(p, stream);
+    if (sr) launch_quant<InT, kModeRHT, true, false>(p, stream);
+    else launch_quant<InT, kModeRHT, false, false>(p, stream);
+  } else if (ragged) {
+    if (sr) launch_quant<InT, kMode1D, true, true>(p, stream);
+    else launch_quant<InT, kMode1D, false, true>(p, stream);
   } else {
-    if (sr) launch_quant<InT, kMode1D, true>(p, stream);
-    else launch_quant<InT, kMode1D, false>(p, stream);
+    if (sr) launch_quant<InT, kMode1D, true, false>(p, stream);
+    else launch_quant<InT, kMode1D, false, false>(p, stream);
   }
 }
 
@@ -411,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void rht_transform_kernel(const InT* __re
   const Tile t = locate(rows, cols);
   if (!t.valid) return;
   float v[16][8];
-  load_sub_tile<InT>(x, ldx, t.r0, t.c0, t.nrows, v);
+  load_sub_tile<InT, false>(x, ldx, t.r0, t.c0, 16, v);
   rht_columns(v, sign_mask);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
