@@ -24,6 +24,14 @@
 // scale, both exact). Keeping the codes, not fp16 values, in LDS moves a
 // quarter of the bytes through it, which is what bounds this loop on gfx950.
 //
+// LDS layout of a stage: codes [256 rows][64 bytes] for A, then B, then the
+// scale bytes [256][8] for A, then B. The four 16-byte chunks of code row r sit
+// at positions chunk ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 2)) & 3, so the
+// fragment reads (one chunk of 16 or 8 consecutive rows per LDS cycle) hit
+// distinct banks. When K % 128 == 0 the codes and scales travel from global
+// memory straight into LDS (gfx950 global_load_lds, 16 and 4 bytes per lane);
+// otherwise they go through registers, with blocks past K read as zero.
+//
 // K order inside a step. MFMA 32x32x16 takes k-slots 0-7 from lanes 0-31 and
 // 8-15 from lanes 32-63. Any assignment of k to (sub-step, slot) works as
 // long as A and B use the same one, so lane half h takes the 64 consecutive
@@ -46,7 +54,7 @@ constexpr int kThreads = 256;
 constexpr int kWaveM = 128;                         // rows of C per wave
 constexpr int kWaveN = 128;                         // columns of C per wave
 constexpr int kStages = 3;                          // LDS ring depth
-constexpr int kCodeStride = kBK / 2 + 16;           // bytes per LDS code row (+16 pad)
+constexpr int kCodeStride = kBK / 2;                // bytes per LDS code row (swizzled)
 constexpr int kScaleStride = kBK / 16;              // bytes per LDS scale row
 constexpr int kCodeBytes = kBM * kCodeStride;       // one operand's codes per stage
 constexpr int kScaleBytes = kBM * kScaleStride;     // one operand's scales per stage
@@ -71,14 +79,12 @@ struct Stage {
   uint2 scales;
 };
 
-// Per-thread addressing of one operand. Rows past the end are clamped to the
-// last row (every load stays in bounds) and get scale 0, which expands their
-// codes to 0.
+// Per-thread addressing of one operand for register staging. Rows past the
+// end are clamped to the last row, so every load stays in bounds; they only
+// feed rows or columns of C that are never stored.
 struct OperandSource {
   const uint8_t* q[4];  // code rows of the 4 chunks (clamped)
   const uint8_t* s;     // scale row (clamped)
-  bool code_valid[4];
-  bool scale_valid;
 };
 
 template <bool k2D>
@@ -91,12 +97,10 @@ __device__ __forceinline__ OperandSource operand_source(const uint8_t* __restric
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t row = row0 + (tid >> 2) + 64 * i;
-    src.code_valid[i] = row < rows;
     const int64_t r = row < rows ? row : rows - 1;
     src.q[i] = q + r * (K >> 1) + 16 * part;
   }
   const int64_t srow = row0 + tid;
-  src.scale_valid = srow < rows;
   const int64_t r = srow < rows ? srow : rows - 1;
   src.s = s + (k2D ? (r >> 4) : r) * (K >> 4);
   return src;
@@ -137,17 +141,86 @@ __device__ __forceinline__ Stage load_stage(const OperandSource& src, int step, 
   return st;
 }
 
-// Writes a stage into LDS (scales of rows past the end become 0 here, when
-// the loaded value is consumed anyway).
+// Position (in 16-byte units) of code chunk c of LDS row r.
+__device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3); }
+
+// Direct-to-LDS staging of one operand's K step (K % 128 == 0). Wave w fills
+// code rows [64w, 64w + 64) with 4 instructions of 16 rows x 64 bytes (lane
+// l: row 16q + l/4, LDS position l % 4, so it loads chunk (l % 4) ^ swz) and
+// scale rows [64w, 64w + 64) with 2 instructions of 32 rows x 8 bytes.
+struct DmaSource {
+  const uint8_t* q[4];  // per instruction: this lane's code chunk at k = 0 (row clamped)
+  const uint8_t* s[2];  // per instruction: this lane's 4 scale bytes at k = 0 (row clamped)
+};
+
+template <bool k2D>
+__device__ __forceinline__ DmaSource dma_source(const uint8_t* __restrict__ q,
+                                                const uint8_t* __restrict__ s, int64_t row0,
+                                                int64_t rows, int64_t K, int wave, int lane) {
+  DmaSource d;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 64 * wave + 16 * i + (lane >> 2);           // row within the tile
+    const int64_t row = row0 + r;
+    const int64_t rc = row < rows ? row : rows - 1;
+    d.q[i] = q + rc * (K >> 1) + 16 * chunk_pos(r, lane & 3);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t row = row0 + 64 * wave + 32 * i + (lane >> 1);
+    const int64_t rc = row < rows ? row : rows - 1;
+    d.s[i] = s + (k2D ? (rc >> 4) : rc) * (K >> 4) + 4 * (lane & 1);
+  }
+  return d;
+}
+
+// One direct-to-LDS load: every lane fetches kBytes from its own global
+// address and the wave's data lands in lane order at LDS byte address
+// lds_addr (taken from M0, which needs one wait state after it is written).
+// Written as inline assembly so that the compiler does not make unrelated LDS
+// reads wait for it; the kernel itself waits for these loads (vmcnt 0) before
+// the barrier that hands a stage to the other waves.
+template <int kBytes>
+__device__ __forceinline__ void lds_dma(const uint8_t* gptr, uint32_t lds_addr) {
+  if constexpr (kBytes == 16) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_addr)
+                 : "memory", "m0");
+  } else {
+    static_assert(kBytes == 4, "4- or 16-byte loads");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_addr)
+                 : "memory", "m0");
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+__device__ __forceinline__ void dma_stage(const DmaSource& d, const uint8_t* codes,
+                                          const uint8_t* scales, int step, int wave) {
+  const int64_t k0 = static_cast<int64_t>(step) * kBK;
+  const uint32_t c0 = lds_address(codes) + 64 * wave * kCodeStride;
+  const uint32_t s0 = lds_address(scales) + 64 * wave * kScaleStride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lds_dma<16>(d.q[i] + (k0 >> 1), c0 + 16 * i * kCodeStride);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) lds_dma<4>(d.s[i] + (k0 >> 4), s0 + 32 * i * kScaleStride);
+}
+
+// Writes a register-staged step into LDS (swizzled code chunks).
 __device__ __forceinline__ void store_stage(uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                            const Stage& st, const OperandSource& src, int tid) {
+                                            const Stage& st, int tid) {
   const int part = tid & 3;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<uint4*>(codes + ((tid >> 2) + 64 * i) * kCodeStride + 16 * part) = st.codes[i];
+    const int r = (tid >> 2) + 64 * i;
+    *reinterpret_cast<uint4*>(codes + r * kCodeStride + 16 * chunk_pos(r, part)) = st.codes[i];
   }
-  const uint2 sc = src.scale_valid ? st.scales : make_uint2(0, 0);
-  *reinterpret_cast<uint2*>(scales + tid * kScaleStride) = sc;
+  *reinterpret_cast<uint2*>(scales + tid * kScaleStride) = st.scales;
 }
 
 // An E4M3 scale byte b as fp16 bits b << 7 is exactly value(b) / 256: the
@@ -178,6 +251,10 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// s_waitcnt immediate that waits for every vector memory load (vmcnt 0) and
+// nothing else (expcnt and lgkmcnt fields at their maximum).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // Scheduling hints (instruction classes of the gfx9 group scheduler).
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedValu = 0x002;
@@ -195,9 +272,10 @@ struct Scales {
   uint32_t b[4];
 };
 
-// Where this lane's fragments sit inside a stage.
+// Where this lane's fragments sit inside a stage ([kHalf] for the code
+// chunks of sub-steps 0-3 and 4-7).
 struct FragOffsets {
-  int a_code, b_code, a_scale, b_scale;
+  int a_code[2], b_code[2], a_scale, b_scale;
 };
 
 template <int kHalf>
@@ -205,9 +283,9 @@ __device__ __forceinline__ void read_codes(Codes& c, const uint8_t* __restrict__
                                            const FragOffsets& o) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    c.a[i][kHalf] = *reinterpret_cast<const uint4*>(stage + o.a_code + i * 32 * kCodeStride + 16 * kHalf);
-    c.b[i][kHalf] = *reinterpret_cast<const uint4*>(stage + kCodeBytes + o.b_code + i * 32 * kCodeStride +
-                                                    16 * kHalf);
+    c.a[i][kHalf] = *reinterpret_cast<const uint4*>(stage + o.a_code[kHalf] + i * 32 * kCodeStride);
+    c.b[i][kHalf] =
+        *reinterpret_cast<const uint4*>(stage + kCodeBytes + o.b_code[kHalf] + i * 32 * kCodeStride);
   }
 }
 
@@ -265,31 +343,53 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const OperandSource src_a = operand_source<kA2D>(p.qa, p.sa, m0, p.M, K, tid);
-  const OperandSource src_b = operand_source<kB2D>(p.qb, p.sb, n0, p.N, K, tid);
-
-  // Prologue: steps 0, 1 and 2 requested together; 0 and 1 go to stages 0
-  // and 1, step 2 stays in flight.
-  const int s1 = 1 < last ? 1 : last;
-  const int s2 = 2 < last ? 2 : last;
-  const Stage a0 = load_stage<kAligned>(src_a, 0, K, part);
-  const Stage b0 = load_stage<kAligned>(src_b, 0, K, part);
-  const Stage a1 = load_stage<kAligned>(src_a, s1, K, part);
-  const Stage b1 = load_stage<kAligned>(src_b, s1, K, part);
-  Stage a_fly = load_stage<kAligned>(src_a, s2, K, part);
-  Stage b_fly = load_stage<kAligned>(src_b, s2, K, part);
-  store_stage(lds, lds + 2 * kCodeBytes, a0, src_a, tid);
-  store_stage(lds + kCodeBytes, lds + 2 * kCodeBytes + kScaleBytes, b0, src_b, tid);
-  store_stage(lds + kStageBytes, lds + kStageBytes + 2 * kCodeBytes, a1, src_a, tid);
-  store_stage(lds + kStageBytes + kCodeBytes, lds + kStageBytes + 2 * kCodeBytes + kScaleBytes, b1,
-              src_b, tid);
+  // Staging state: DMA addressing (kAligned) or register staging.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  DmaSource dma_a, dma_b;
+  OperandSource src_a, src_b;
+  Stage a_fly, b_fly;
+  if constexpr (kAligned) {
+    // Prologue: steps 0 and 1 into stages 0 and 1.
+    dma_a = dma_source<kA2D>(p.qa, p.sa, m0, p.M, K, wave_u, lane);
+    dma_b = dma_source<kB2D>(p.qb, p.sb, n0, p.N, K, wave_u, lane);
+    dma_stage(dma_a, lds, lds + 2 * kCodeBytes, 0, wave_u);
+    dma_stage(dma_b, lds + kCodeBytes, lds + 2 * kCodeBytes + kScaleBytes, 0, wave_u);
+    if (nsteps > 1) {
+      uint8_t* st = lds + kStageBytes;
+      dma_stage(dma_a, st, st + 2 * kCodeBytes, 1, wave_u);
+      dma_stage(dma_b, st + kCodeBytes, st + 2 * kCodeBytes + kScaleBytes, 1, wave_u);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  } else {
+    // Prologue: steps 0, 1 and 2 requested together; 0 and 1 go to stages 0
+    // and 1, step 2 stays in flight.
+    src_a = operand_source<kA2D>(p.qa, p.sa, m0, p.M, K, tid);
+    src_b = operand_source<kB2D>(p.qb, p.sb, n0, p.N, K, tid);
+    const int s1 = 1 < last ? 1 : last;
+    const int s2 = 2 < last ? 2 : last;
+    const Stage a0 = load_stage<kAligned>(src_a, 0, K, part);
+    const Stage b0 = load_stage<kAligned>(src_b, 0, K, part);
+    const Stage a1 = load_stage<kAligned>(src_a, s1, K, part);
+    const Stage b1 = load_stage<kAligned>(src_b, s1, K, part);
+    a_fly = load_stage<kAligned>(src_a, s2, K, part);
+    b_fly = load_stage<kAligned>(src_b, s2, K, part);
+    store_stage(lds, lds + 2 * kCodeBytes, a0, tid);
+    store_stage(lds + kCodeBytes, lds + 2 * kCodeBytes + kScaleBytes, b0, tid);
+    store_stage(lds + kStageBytes, lds + kStageBytes + 2 * kCodeBytes, a1, tid);
+    store_stage(lds + kStageBytes + kCodeBytes, lds + kStageBytes + 2 * kCodeBytes + kScaleBytes, b1,
+                tid);
+  }
   __syncthreads();
 
   const int frag_row = lane & 31;
   const int half = lane >> 5;
+  const int swz = ((frag_row >> 1) ^ (frag_row >> 2)) & 3;  // same for frag_row + 32 i
   FragOffsets o;
-  o.a_code = (wm * kWaveM + frag_row) * kCodeStride + 32 * half;
-  o.b_code = (wn * kWaveN + frag_row) * kCodeStride + 32 * half;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    o.a_code[h] = (wm * kWaveM + frag_row) * kCodeStride + 16 * ((2 * half + h) ^ swz);
+    o.b_code[h] = (wn * kWaveN + frag_row) * kCodeStride + 16 * ((2 * half + h) ^ swz);
+  }
   o.a_scale = (wm * kWaveM + frag_row) * kScaleStride + 4 * half;
   o.b_scale = (wn * kWaveN + frag_row) * kScaleStride + 4 * half;
 
@@ -298,7 +398,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   // of step s + 1). The codes of step s + 1 are read from LDS as soon as the
   // ones they replace are dead: the sub-step 0-3 halves after sub-step 2,
   // the 4-7 halves in sub-step 7. Stage s + 1 was written in step s - 1,
-  // before the barrier that ended it.
+  // before the barrier that ended it (DMA: requested at the start of step
+  // s - 1 and waited for before that barrier).
   Codes c;
   Scales sc, sc_next;
   read_codes<0>(c, lds, o);
@@ -325,15 +426,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       } else {
         expand_substep(af[0], bf[0], c, sc_next, 0);  // step s + 1, sub-step 0
       }
-      if (kk == 1) {
-        // step s + 2 (loaded during step s - 1) into the stage that held
-        // step s - 1, then request step s + 3
-        uint8_t* st = lds + wr * kStageBytes;
-        store_stage(st, st + 2 * kCodeBytes, a_fly, src_a, tid);
-        store_stage(st + kCodeBytes, st + 2 * kCodeBytes + kScaleBytes, b_fly, src_b, tid);
-        const int ld = (step + 3) < last ? (step + 3) : last;
-        a_fly = load_stage<kAligned>(src_a, ld, K, part);
-        b_fly = load_stage<kAligned>(src_b, ld, K, part);
+      if constexpr (kAligned) {
+        if (kk == 0) {
+          // step s + 2 straight into the stage that held step s - 1 (past
+          // the end: the last step again, into a stage nobody reads; no
+          // branch, so the region stays one block for the scheduler)
+          uint8_t* st = lds + wr * kStageBytes;
+          const int ld = (step + 2) < last ? (step + 2) : last;
+          dma_stage(dma_a, st, st + 2 * kCodeBytes, ld, wave_u);
+          dma_stage(dma_b, st + kCodeBytes, st + 2 * kCodeBytes + kScaleBytes, ld, wave_u);
+        }
+      } else {
+        if (kk == 1) {
+          // step s + 2 (loaded during step s - 1) into the stage that held
+          // step s - 1, then request step s + 3
+          uint8_t* st = lds + wr * kStageBytes;
+          store_stage(st, st + 2 * kCodeBytes, a_fly, tid);
+          store_stage(st + kCodeBytes, st + 2 * kCodeBytes + kScaleBytes, b_fly, tid);
+          const int ld = (step + 3) < last ? (step + 3) : last;
+          a_fly = load_stage<kAligned>(src_a, ld, K, part);
+          b_fly = load_stage<kAligned>(src_b, ld, K, part);
+        }
       }
       if (kk == 3) {
         read_codes<0>(c, next_stage, o);
@@ -349,6 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
 #endif
     }
+    if constexpr (kAligned) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     sc = sc_next;
     cur = nxt;
