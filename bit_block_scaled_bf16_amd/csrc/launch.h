@@ -47,6 +47,10 @@ struct GemmLaunch {
 
 int launch_gemm(const GemmLaunch& g, hipStream_t stream);
 
+// Compute units of the current device (queried once per device; 0 if the
+// query fails).
+int device_compute_units();
+
 int launch_philox_fill(uint64_t seed, uint32_t c2, uint32_t c3, int64_t n_groups, uint32_t* out,
                        hipStream_t stream);
 

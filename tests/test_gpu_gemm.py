@@ -51,8 +51,14 @@ def check(c_gpu, ref, absref, k, bf16=True):
     return fro
 
 
+# Shapes up to a quarter of the CUs' worth of 256 x 256 tiles run entirely as
+# 128 x 128 tiles; (2500, 2600, 208) runs entirely as 256 x 256 tiles with
+# ragged edges and a ragged K; (4100 | 4312, 4080, *) give 272 tiles, i.e. one
+# full round of 256 x 256 tiles plus a last round of 128 x 128 quarters on
+# 256 CUs, including quarters partly or wholly past the ragged edges.
 @pytest.mark.parametrize("m,n,k", [(16, 16, 16), (256, 256, 64), (300, 520, 80), (512, 768, 1024),
-                                   (33, 47, 208), (272, 256, 5120)])
+                                   (33, 47, 208), (272, 256, 5120), (2500, 2608, 208),
+                                   (4312, 4080, 336), (4100, 4080, 384)])
 @pytest.mark.parametrize("b_2d", [False, True])
 def test_gemm_parity(m, n, k, b_2d):
     torch = require_gpu()
