@@ -69,15 +69,16 @@ class Step:
         bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
         self.x, self.w, self.dy = bf(x_np), bf(w_np), bf(dy_np)
         sc = lambda: torch.zeros(4, dtype=torch.float32, device=dev)
+        ws = lambda: nv.amax_workspace(dev)
         e = lambda *s: torch.empty(s, dtype=u8, device=dev)
         # X row copy (fprop A)
-        self.qx, self.sx, self.tx, self.ax = e(t, h // 2), e(t, h // 16), sc(), sc()
+        self.qx, self.sx, self.tx, self.ax = e(t, h // 2), e(t, h // 16), sc(), ws()
         # W 16x16: W and W^T codes, grid and grid^T
         self.qw, self.sw, self.qwt, self.swt = e(f, h // 2), e(f // 16, h // 16), e(h, f // 2), e(h // 16, f // 16)
-        self.tw, self.aw = sc(), sc()
+        self.tw, self.aw = sc(), ws()
         # RHT copies (wgrad operands), stored [cols][tokens/2]
-        self.qdy, self.sdy, self.tdy, self.ady = e(f, t // 2), e(f, t // 16), sc(), sc()
-        self.qxt, self.sxt, self.txt, self.axt = e(h, t // 2), e(h, t // 16), sc(), sc()
+        self.qdy, self.sdy, self.tdy, self.ady = e(f, t // 2), e(f, t // 16), sc(), ws()
+        self.qxt, self.sxt, self.txt, self.axt = e(h, t // 2), e(h, t // 16), sc(), ws()
         self.y = torch.empty((t, f), dtype=torch.bfloat16, device=dev)
         self.dw = torch.empty((f, h), dtype=torch.bfloat16, device=dev)
         self.status = torch.zeros(4, dtype=torch.int32, device=dev)

@@ -18,6 +18,7 @@ from dataclasses import dataclass
 
 from . import _lib
 from ._lib import (  # noqa: F401  (re-exported constants and raw entry points)
+    AMAX_WS_BYTES,
     BF16,
     BLOCK_1D,
     BLOCK_2D,
@@ -75,6 +76,14 @@ def _scalar(device):
     return torch.zeros(4, dtype=torch.float32, device=device)
 
 
+def amax_workspace(device):
+    """A workspace for the tensor amax of one quantize call (its element 0
+    holds the amax afterwards)."""
+    import torch
+
+    return torch.zeros(AMAX_WS_BYTES // 4, dtype=torch.float32, device=device)
+
+
 def quantize(x, block: int = BLOCK_1D, rounding: int = ROUND_RN, seed: int = 0, offset: int = 0,
              outputs: int = OUT_ROW | OUT_COL, amax=None, dev_status=None):
     """Quantizes x [rows, cols] (bf16 or float32, device).
@@ -87,7 +96,7 @@ def quantize(x, block: int = BLOCK_1D, rounding: int = ROUND_RN, seed: int = 0, 
     rows, cols = x.shape
     dev = x.device
     scale = _scalar(dev)
-    ws = None if amax is not None else _scalar(dev)
+    ws = None if amax is not None else amax_workspace(dev)
     row = col = None
     q_row = s_row = q_col = s_col = None
     two_d = block == BLOCK_2D
@@ -115,7 +124,7 @@ def rht_quantize(x, rht_seed: int, rounding: int = ROUND_RN, seed: int = 0, offs
     tokens, cols = x.shape
     dev = x.device
     scale = _scalar(dev)
-    ws = None if amax is not None else _scalar(dev)
+    ws = None if amax is not None else amax_workspace(dev)
     q = _empty((cols, tokens // 2), torch.uint8, dev)
     s = _empty((cols, tokens // 16), torch.uint8, dev)
     nvfp4_rht_quantize(x, rht_seed, rounding, seed, offset, amax, ws, q, s, scale, dev_status)

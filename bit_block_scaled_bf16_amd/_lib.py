@@ -43,6 +43,9 @@ _SIGNATURES = {
 
 EXPORTED = tuple(_SIGNATURES)
 
+# Bytes of the amax workspace (NVFP4_AMAX_WS_BYTES in include/nvfp4.h).
+AMAX_WS_BYTES = 16384
+
 _lib = None
 
 
@@ -72,6 +75,16 @@ def lib() -> ctypes.CDLL:
 def _ptr(t) -> int | None:
     if t is None:
         return None
+    return t.data_ptr()
+
+
+def _ws(t) -> int | None:
+    """Pointer of an amax workspace, which must hold AMAX_WS_BYTES (the
+    library would write past a smaller one)."""
+    if t is None:
+        return None
+    if t.numel() * t.element_size() < AMAX_WS_BYTES or not t.is_contiguous():
+        raise ValueError(f"amax workspace must be a contiguous buffer of >= {AMAX_WS_BYTES} bytes")
     return t.data_ptr()
 
 
@@ -116,7 +129,7 @@ def nvfp4_quantize(x, block, rounding, seed, offset, outputs, amax_in, amax_ws, 
     rows, cols = x.shape
     _check("nvfp4_quantize", lib().nvfp4_quantize(
         _ptr(x), _dtype_code(x), rows, cols, _ld(x), block, rounding, seed, offset, outputs,
-        _ptr(amax_in), _ptr(amax_ws), _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col),
+        _ptr(amax_in), _ws(amax_ws), _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col),
         _ptr(tensor_scale), _ptr(dev_status), _stream(stream)))
 
 
@@ -125,7 +138,7 @@ def nvfp4_rht_quantize(x, rht_seed, rounding, seed, offset, amax_in, amax_ws, q_
     tokens, cols = x.shape
     _check("nvfp4_rht_quantize", lib().nvfp4_rht_quantize(
         _ptr(x), _dtype_code(x), tokens, cols, _ld(x), rht_seed, rounding, seed, offset,
-        _ptr(amax_in), _ptr(amax_ws), _ptr(q_t), _ptr(s_t), _ptr(tensor_scale),
+        _ptr(amax_in), _ws(amax_ws), _ptr(q_t), _ptr(s_t), _ptr(tensor_scale),
         _ptr(dev_status), _stream(stream)))
 
 

@@ -23,6 +23,7 @@
 // staged in LDS so each column's 128 bytes leave as contiguous stores.
 #include "device_common.h"
 #include "launch.h"
+#include "nvfp4.h"
 
 namespace nvfp4 {
 namespace {
@@ -31,7 +32,7 @@ constexpr int kThreads = 256;
 constexpr int kTileRows = 256;
 constexpr int kTileCols = 128;
 constexpr int kLdsCodeStride = kTileRows / 2 + 8;  // bytes per staged column (+8 pad)
-constexpr int kLdsScaleStride = kTileRows / 16 + 1;
+constexpr int64_t kMaxTileBlocks = 512;  // workgroups of the tile-shaped amax kernel
 
 enum Mode { kMode1D = 0, kMode2D = 1, kModeRHT = 2 };
 
@@ -43,7 +44,7 @@ struct Tile {
   bool valid;
 };
 
-__device__ __forceinline__ Tile locate(int64_t rows, int64_t cols) {
+__device__ __forceinline__ Tile locate_tile(int64_t tile, int64_t rows, int64_t cols) {
   Tile t;
   const int tid = threadIdx.x;
   t.lane = tid & 63;
@@ -51,13 +52,32 @@ __device__ __forceinline__ Tile locate(int64_t rows, int64_t cols) {
   t.cg = t.lane & 15;
   t.rg = t.lane >> 4;
   const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
-  t.tr = static_cast<int64_t>(blockIdx.x) / tiles_c;
-  t.tc = static_cast<int64_t>(blockIdx.x) - t.tr * tiles_c;
+  t.tr = tile / tiles_c;
+  t.tc = tile - t.tr * tiles_c;
   t.r0 = t.tr * kTileRows + t.wave * 64 + t.rg * 16;
   t.c0 = t.tc * kTileCols + t.cg * 8;
   t.valid = (t.r0 < rows) && (t.c0 < cols);
   t.nrows = (rows - t.r0) < 16 ? static_cast<int>(rows - t.r0) : 16;
   return t;
+}
+
+// Workgroups are handed to the 8 XCDs of the chip round-robin (workgroup b
+// to XCD b % 8), and each XCD has its own L2. Numbering the tiles so that XCD
+// x gets a contiguous run of them puts horizontally adjacent tiles, which
+// write the two halves of the same 128-byte lines of the row copy, behind
+// the same L2, where the halves merge before they reach memory. The mapping
+// is a permutation of [0, ntiles) for any tile count.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t ntiles) {
+  const int64_t q = ntiles / kXcds, r = ntiles - q * kXcds;
+  const int64_t x = b % kXcds, j = b / kXcds;
+  return x * q + (x < r ? x : r) + j;
+}
+
+__device__ __forceinline__ Tile locate(int64_t rows, int64_t cols) {
+  const int64_t ntiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
+  return locate_tile(xcd_tile(static_cast<int64_t>(blockIdx.x), ntiles), rows, cols);
 }
 
 // Loads this lane's 16 x 8 values as float32 (bf16 widened exactly).
@@ -123,9 +143,18 @@ __device__ __forceinline__ void rht_columns(float (&v)[16][8], uint32_t sign_mas
   }
 }
 
-// Block-wide max of per-thread values, then one atomic max into *dst (the
-// float bits of a non-negative amax order like unsigned integers).
-__device__ __forceinline__ void block_max_to_global(uint32_t m, uint32_t* lds4, float* dst) {
+// Workspace of the tensor amax (floats): [0] receives the amax, the
+// per-workgroup partial maxima (float bits, which order like unsigned
+// integers for non-negative values, NaN above infinity) start at
+// kPartialsOffset. Partials instead of one atomic maximum need no zeroed
+// word before the reduction, so a call is two kernels, not three.
+constexpr int kPartialsOffset = 64;
+constexpr int kMaxPartials = 1024;
+static_assert(kPartialsOffset + kMaxPartials <= NVFP4_AMAX_WS_BYTES / 4, "workspace size");
+static_assert(kMaxTileBlocks <= kMaxPartials, "one partial per workgroup");
+
+// Block-wide max of per-thread values, written by thread 0 to *dst.
+__device__ __forceinline__ void block_max_store(uint32_t m, uint32_t* lds4, uint32_t* dst) {
   m = wave_max_u32(m);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) lds4[wave] = m;
@@ -134,37 +163,182 @@ __device__ __forceinline__ void block_max_to_global(uint32_t m, uint32_t* lds4, 
     uint32_t r = lds4[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) r = (lds4[w] > r) ? lds4[w] : r;
-    atomicMax(reinterpret_cast<unsigned int*>(dst), r);
+    *dst = r;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Tensor amax (optionally of the Hadamard-transformed tensor).
+// Tensor amax.
 // ---------------------------------------------------------------------------
-template <typename InT, bool kRht, bool kRagged>
-__global__ __launch_bounds__(kThreads) void amax_kernel(const InT* __restrict__ x, int64_t rows,
-                                                        int64_t cols, int64_t ldx,
-                                                        uint32_t sign_mask, float* amax_out) {
+
+// Contiguous input (ldx == cols), no transform: a flat stream of 16-byte
+// nontemporal loads (the data is not reused from the cache), 8 per thread in
+// flight per iteration. bf16 magnitudes are compared
+// two at a time as packed 16-bit integers (the bf16 bits of |x| order like
+// its value, NaN above infinity).
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+constexpr int kFlatUnroll = 8;
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, a),
+                                                                __builtin_bit_cast(ushort2_t, b)));
+}
+
+template <typename InT>
+__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* __restrict__ x, int64_t n,
+                                                             uint32_t* __restrict__ partials) {
   __shared__ uint32_t lds4[kThreads / 64];
-  const Tile t = locate(rows, cols);
-  uint32_t m = 0;
-  if (t.valid) {
-    float v[16][8];
-    load_sub_tile<InT, kRagged>(x, ldx, t.r0, t.c0, t.nrows, v);
-    if constexpr (kRht) rht_columns(v, sign_mask);
+  constexpr int kVec = 16 / sizeof(InT);  // elements per 16-byte load
+  const int64_t nvec = n / kVec;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads * kFlatUnroll;
+  uint32_t m = 0;  // bf16: two packed 16-bit maxima; float32: one
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * kFlatUnroll + threadIdx.x;
+       base < nvec; base += stride) {
+    uint4 r[kFlatUnroll];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int u = 0; u < kFlatUnroll; ++u) {
+      const int64_t i = base + u * kThreads;
+      r[u] = i < nvec ? load_stream(xv + i) : make_uint4(0u, 0u, 0u, 0u);
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t b = abs_bits(v[i][j]);
-        m = (b > m) ? b : m;
+    for (int u = 0; u < kFlatUnroll; ++u) {
+      const uint32_t w[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (sizeof(InT) == 2) {
+          m = max_u16x2(m, w[k] & 0x7FFF7FFFu);
+        } else {
+          const uint32_t a = w[k] & 0x7FFFFFFFu;
+          m = a > m ? a : m;
+        }
       }
+    }
   }
-  block_max_to_global(m, lds4, amax_out);
+  // the last n % kVec elements
+  if (blockIdx.x == 0 && threadIdx.x < n - nvec * kVec) {
+    if constexpr (sizeof(InT) == 2) {
+      m = max_u16x2(m, static_cast<uint32_t>(x[nvec * kVec + threadIdx.x]) & 0x7FFFu);
+    } else {
+      const uint32_t a = __float_as_uint(x[nvec * kVec + threadIdx.x]) & 0x7FFFFFFFu;
+      m = a > m ? a : m;
+    }
+  }
+  if constexpr (sizeof(InT) == 2) {
+    const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+    m = (lo > hi ? lo : hi) << 16;  // float bits of the larger bf16 magnitude
+  }
+  block_max_store(m, lds4, partials + blockIdx.x);
 }
 
-__global__ void fill_f32_kernel(float* p, float v) {
-  if (threadIdx.x == 0) *p = v;
+// Tile-shaped amax (the Hadamard transform needs whole 16-token columns; a
+// padded input needs its row stride): each workgroup walks tiles
+// blockIdx.x, blockIdx.x + gridDim.x, ... For bf16 the next tile's 16 x 16
+// bytes are requested before the current one is transformed, and the
+// transform goes one pair of columns at a time (32 floats live).
+template <bool kRht>
+__device__ __forceinline__ uint32_t absmax_bf16_tile(const uint4 (&raw)[16], uint32_t sign_mask,
+                                                     uint32_t m) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float c0[16], c1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t w = k == 0 ? raw[i].x : k == 1 ? raw[i].y : k == 2 ? raw[i].z : raw[i].w;
+      c0[i] = bf16_lo(w);
+      c1[i] = bf16_hi(w);
+    }
+    if constexpr (kRht) {
+      rht16(c0, sign_mask);
+      rht16(c1, sign_mask);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t b0 = abs_bits(c0[i]), b1 = abs_bits(c1[i]);
+      m = (b0 > m) ? b0 : m;
+      m = (b1 > m) ? b1 : m;
+    }
+  }
+  return m;
+}
+
+template <bool kRagged>
+__device__ __forceinline__ void load_raw_bf16(const uint16_t* __restrict__ x, int64_t ldx,
+                                              const Tile& t, uint4 (&raw)[16]) {
+  const uint16_t* row = x + t.r0 * ldx + t.c0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    raw[i] = (t.valid && (!kRagged || i < t.nrows)) ? load_stream(row) : make_uint4(0u, 0u, 0u, 0u);
+    row += ldx;
+  }
+}
+
+template <typename InT, bool kRht, bool kRagged>
+__global__ __launch_bounds__(kThreads) void amax_tile_kernel(const InT* __restrict__ x, int64_t rows,
+                                                             int64_t cols, int64_t ldx,
+                                                             uint32_t sign_mask, int64_t tiles,
+                                                             uint32_t* __restrict__ partials) {
+  __shared__ uint32_t lds4[kThreads / 64];
+  uint32_t m = 0;
+  if constexpr (sizeof(InT) == 2) {
+    // invalid lanes (past the columns) load zeros, which leave the max alone
+    int64_t tile = blockIdx.x;
+    uint4 raw[16];
+    load_raw_bf16<kRagged>(x, ldx, locate_tile(tile, rows, cols), raw);
+    for (; tile < tiles; tile += gridDim.x) {
+      uint4 cur[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cur[i] = raw[i];
+      const int64_t next = tile + gridDim.x;
+      if (next < tiles) load_raw_bf16<kRagged>(x, ldx, locate_tile(next, rows, cols), raw);
+      m = absmax_bf16_tile<kRht>(cur, sign_mask, m);
+    }
+  } else {
+    for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+      const Tile t = locate_tile(tile, rows, cols);
+      if (!t.valid) continue;
+      float v[16][8];
+      load_sub_tile<InT, kRagged>(x, ldx, t.r0, t.c0, t.nrows, v);
+      if constexpr (kRht) rht_columns(v, sign_mask);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t b = abs_bits(v[i][j]);
+          m = (b > m) ? b : m;
+        }
+    }
+  }
+  block_max_store(m, lds4, partials + blockIdx.x);
+}
+
+// The tensor amax from n <= kMaxPartials partial maxima. Each wave reduces
+// them on its own (4 loads of 16 bytes per lane and a wave maximum: no LDS,
+// no barrier). Entries past n hold stale values and are masked off.
+__device__ __forceinline__ float reduce_partials(const uint32_t* __restrict__ partials, int n) {
+  const int lane = threadIdx.x & 63;
+  const uint4* p4 = reinterpret_cast<const uint4*>(partials);
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxPartials / 256; ++k) {
+    const int i = 4 * (lane + 64 * k);
+    if (i < n) {
+      const uint4 b = p4[lane + 64 * k];
+      const uint32_t v[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t x = i + c < n ? v[c] : 0u;
+        m = x > m ? x : m;
+      }
+    }
+  }
+  return __uint_as_float(wave_max_u32(m));
 }
 
 // Writes the tensor scale (and the status) for an empty tensor.
@@ -175,7 +349,7 @@ __global__ void empty_tensor_kernel(const float* amax_in, float* amax_ws, float*
   if (amax_in != nullptr) {
     a = *amax_in;
   } else {
-    *amax_ws = 0.0f;
+    *amax_ws = 0.0f;  // [0] of the workspace: the tensor amax
   }
   *tensor_scale = tensor_scale_from_amax(a);
   if (!(a <= 3.402823466e38f) && dev_status != nullptr) *dev_status = 1;
@@ -187,7 +361,10 @@ __global__ void empty_tensor_kernel(const float* amax_in, float* amax_ws, float*
 struct QuantParams {
   const void* x;
   int64_t rows, cols, ldx;
-  const float* amax;  // caller's amax or the workspace the amax kernel filled
+  const float* amax_in;       // caller's amax, or NULL: reduce the partials
+  const uint32_t* partials;   // per-workgroup maxima of the amax kernel
+  int n_partials;
+  float* amax_out;            // receives the reduced amax (workspace [0]), or NULL
   float* tensor_scale;
   int32_t* dev_status;
   uint8_t* q_row;
@@ -229,168 +406,259 @@ __device__ __forceinline__ void column_block(const float (&col)[16], float six_s
   sbyte = bs.byte;
 }
 
+// One lane's 16 x 8 register tile as loaded (bf16 words or float32 values),
+// read back as float32 value by value: only the values a step needs are
+// widened, which keeps the register count (and so the waves per SIMD that
+// hide the load latency) where it is with the raw words alone.
+template <typename InT>
+struct RawTile;
+
+template <>
+struct RawTile<uint16_t> {
+  uint4 r[16];
+  __device__ __forceinline__ float get(int i, int j) const {
+    const uint32_t w = (j >> 1) == 0 ? r[i].x : (j >> 1) == 1 ? r[i].y : (j >> 1) == 2 ? r[i].z : r[i].w;
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+  // float32 bits of the largest magnitude (packed 16-bit maxima of the bf16
+  // magnitudes, then the larger half)
+  __device__ __forceinline__ uint32_t absmax_bits() const {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      m = max_u16x2(m, r[i].x & 0x7FFF7FFFu);
+      m = max_u16x2(m, r[i].y & 0x7FFF7FFFu);
+      m = max_u16x2(m, r[i].z & 0x7FFF7FFFu);
+      m = max_u16x2(m, r[i].w & 0x7FFF7FFFu);
+    }
+    const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+    return (lo > hi ? lo : hi) << 16;
+  }
+};
+
+template <>
+struct RawTile<float> {
+  float4 r[16][2];
+  __device__ __forceinline__ float get(int i, int j) const {
+    const float4& v = r[i][j >> 2];
+    return (j & 3) == 0 ? v.x : (j & 3) == 1 ? v.y : (j & 3) == 2 ? v.z : v.w;
+  }
+  __device__ __forceinline__ uint32_t absmax_bits() const {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t b = abs_bits(get(i, j));
+        m = b > m ? b : m;
+      }
+    return m;
+  }
+};
+
+// Loads this lane's 16 x 8 values. Lanes past the matrix, and with kRagged
+// the rows at or beyond r0 + nrows (a row count that is not a multiple of 16,
+// allowed only for the row-blocked copy), read as zero.
+template <typename InT, bool kRagged>
+__device__ __forceinline__ void load_raw(const InT* __restrict__ x, int64_t ldx, const Tile& t,
+                                         RawTile<InT>& raw) {
+  const InT* row = x + t.r0 * ldx + t.c0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool ok = t.valid && (!kRagged || i < t.nrows);
+    if constexpr (sizeof(InT) == 2) {
+      raw.r[i] = ok ? *reinterpret_cast<const uint4*>(row) : make_uint4(0u, 0u, 0u, 0u);
+    } else {
+      raw.r[i][0] = ok ? *reinterpret_cast<const float4*>(row) : make_float4(0.f, 0.f, 0.f, 0.f);
+      raw.r[i][1] = ok ? *reinterpret_cast<const float4*>(row + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    row += ldx;
+  }
+}
+
+// LDS staging of the tile's outputs that leave in another shape than they
+// are computed: the column copy (codes and scales of each column) and the
+// row-block scales of the 1x16 row copy (8 bytes per row, one 8-byte store
+// instead of eight byte stores).
+struct Staging {
+  uint8_t codes[kTileCols * kLdsCodeStride];
+  uint8_t col_scales[kTileCols * 16];
+  uint8_t row_scales[kTileRows * 8];
+};
+
+// One workgroup per 256 x 128 tile.
 template <typename InT, int kMode, bool kSR, bool kRagged>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_codes[kTileCols * kLdsCodeStride];
-  __shared__ uint8_t lds_scales[kTileCols * kLdsScaleStride];
+  __shared__ __attribute__((aligned(16))) Staging st;
 
   const int64_t rows = p.rows, cols = p.cols;
-  const Tile t = locate(rows, cols);
-  const float amax = *p.amax;
+  const float amax = p.amax_in != nullptr ? *p.amax_in : reduce_partials(p.partials, p.n_partials);
   const float s = tensor_scale_from_amax(amax);
   const float six_s = __fmul_rn(6.0f, s);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *p.tensor_scale = s;
+    if (p.amax_out != nullptr) *p.amax_out = amax;
     if (!(amax <= 3.402823466e38f) && p.dev_status != nullptr) *p.dev_status = 1;
   }
   const bool out_row = (p.outputs & 1) != 0 && kMode != kModeRHT;
   const bool out_col = (p.outputs & 2) != 0 || kMode == kModeRHT;
-  const int c_local0 = t.cg * 8;
-  const int r_local = t.wave * 64 + t.rg * 16;
+  const bool stage_row_scales = out_row && kMode != kMode2D;
+  const Tile t = locate(rows, cols);
+  RawTile<InT> cur;
+  load_raw<InT, kRagged>(static_cast<const InT*>(p.x), p.ldx, t, cur);
+  {
+    const int c_local0 = t.cg * 8;
+    const int r_local = t.wave * 64 + t.rg * 16;
 
-  if (t.valid) {
-    float v[16][8];
-    load_sub_tile<InT, kRagged>(static_cast<const InT*>(p.x), p.ldx, t.r0, t.c0, t.nrows, v);
-    if constexpr (kMode == kModeRHT) rht_columns(v, p.sign_mask);
-
-    if constexpr (kMode == kMode2D) {
-      // one scale per 16x16 tile: this lane's half and lane ^ 1's half
-      uint32_t am = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t b = abs_bits(v[i][j]);
-          am = (b > am) ? b : am;
+    if (t.valid) {
+      if constexpr (kMode == kMode2D) {
+        // one scale per 16x16 tile: this lane's half and lane ^ 1's half
+        uint32_t am = cur.absmax_bits();
+        const uint32_t other = swap_adjacent_lanes(am);
+        am = (other > am) ? other : am;
+        const BlockScale bs = block_scale(__uint_as_float(am), six_s, s);
+        // codes of a zero-scale tile are 0 (a mask, not a branch)
+        const uint32_t keep = (bs.byte == 0u) ? 0u : 0xFFFFFFFFu;
+        if ((t.cg & 1) == 0) {
+          if (out_row) p.s_row[(t.r0 >> 4) * (cols >> 4) + (t.c0 >> 4)] = static_cast<uint8_t>(bs.byte);
+          if (out_col) p.s_col[(t.c0 >> 4) * (rows >> 4) + (t.r0 >> 4)] = static_cast<uint8_t>(bs.byte);
         }
-      const uint32_t other = swap_adjacent_lanes(am);
-      am = (other > am) ? other : am;
-      const BlockScale bs = block_scale(__uint_as_float(am), six_s, s);
+        if (out_row) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[i][j] = __fmul_rn(v[i][j], bs.mult);
-      // codes of a zero-scale tile are 0 (a mask, not a branch)
-      const uint32_t keep = (bs.byte == 0u) ? 0u : 0xFFFFFFFFu;
-      if ((t.cg & 1) == 0) {
-        if (out_row) p.s_row[(t.r0 >> 4) * (cols >> 4) + (t.c0 >> 4)] = static_cast<uint8_t>(bs.byte);
-        if (out_col) p.s_col[(t.c0 >> 4) * (rows >> 4) + (t.r0 >> 4)] = static_cast<uint8_t>(bs.byte);
-      }
-      if (out_row) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t w = pack8_rn(v[i]) & keep;
-          *reinterpret_cast<uint32_t*>(p.q_row + (t.r0 + i) * (cols >> 1) + (t.c0 >> 1)) = w;
-        }
-      }
-      if (out_col) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float col[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) col[i] = v[i][j];
-          const uint32_t w0 = pack8_rn(col) & keep;
-          const uint32_t w1 = pack8_rn(col + 8) & keep;
-          uint32_t* dst = reinterpret_cast<uint32_t*>(lds_codes + (c_local0 + j) * kLdsCodeStride +
-                                                      (r_local >> 1));
-          dst[0] = w0;
-          dst[1] = w1;
-        }
-      }
-    } else {
-      if (out_row) {
-        // 1x16 blocks along the row: this lane's 8 values + lane ^ 1's 8.
-        // Rows past a ragged end are skipped by a predicate (the same for
-        // both lanes of a pair), not a loop exit, so the register tile keeps
-        // static indices.
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (!kRagged || i < t.nrows) {
-            uint32_t am = 0;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const uint32_t b = abs_bits(v[i][j]);
-              am = (b > am) ? b : am;
-            }
-            const uint32_t other = swap_adjacent_lanes(am);
-            am = (other > am) ? other : am;
-            const BlockScale bs = block_scale(__uint_as_float(am), six_s, s);
+          for (int i = 0; i < 16; ++i) {
             float y[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) y[j] = __fmul_rn(v[i][j], bs.mult);
-            uint32_t w;
-            if constexpr (kSR) {
-              const uint64_t e = static_cast<uint64_t>(t.r0 + i) * static_cast<uint64_t>(cols) +
-                                 static_cast<uint64_t>(t.c0);
-              w = pack8_sr(y, sr_words(p.k0, p.k1, e >> 3, p.offset, kStreamRow));
-            } else {
-              w = pack8_rn(y);
-            }
-            w &= (bs.byte == 0u) ? 0u : 0xFFFFFFFFu;
+            for (int j = 0; j < 8; ++j) y[j] = __fmul_rn(cur.get(i, j), bs.mult);
+            const uint32_t w = pack8_rn(y) & keep;
             *reinterpret_cast<uint32_t*>(p.q_row + (t.r0 + i) * (cols >> 1) + (t.c0 >> 1)) = w;
-            if ((t.cg & 1) == 0) {
-              p.s_row[(t.r0 + i) * (cols >> 4) + (t.c0 >> 4)] = static_cast<uint8_t>(bs.byte);
+          }
+        }
+        if (out_col) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float col[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) col[i] = __fmul_rn(cur.get(i, j), bs.mult);
+            uint32_t* dst = reinterpret_cast<uint32_t*>(st.codes + (c_local0 + j) * kLdsCodeStride +
+                                                        (r_local >> 1));
+            dst[0] = pack8_rn(col) & keep;
+            dst[1] = pack8_rn(col + 8) & keep;
+          }
+        }
+      } else {
+        if (out_row) {
+          // 1x16 blocks along the row: this lane's 8 values + lane ^ 1's 8.
+          // Rows past a ragged end are skipped by a predicate (the same for
+          // both lanes of a pair), not a loop exit.
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            if (!kRagged || i < t.nrows) {
+              uint32_t am = 0;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const uint32_t b = abs_bits(cur.get(i, j));
+                am = (b > am) ? b : am;
+              }
+              const uint32_t other = swap_adjacent_lanes(am);
+              am = (other > am) ? other : am;
+              const BlockScale bs = block_scale(__uint_as_float(am), six_s, s);
+              float y[8];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) y[j] = __fmul_rn(cur.get(i, j), bs.mult);
+              uint32_t w;
+              if constexpr (kSR) {
+                const uint64_t e = static_cast<uint64_t>(t.r0 + i) * static_cast<uint64_t>(cols) +
+                                   static_cast<uint64_t>(t.c0);
+                w = pack8_sr(y, sr_words(p.k0, p.k1, e >> 3, p.offset, kStreamRow));
+              } else {
+                w = pack8_rn(y);
+              }
+              w &= (bs.byte == 0u) ? 0u : 0xFFFFFFFFu;
+              *reinterpret_cast<uint32_t*>(p.q_row + (t.r0 + i) * (cols >> 1) + (t.c0 >> 1)) = w;
+              if ((t.cg & 1) == 0) st.row_scales[(r_local + i) * 8 + (t.cg >> 1)] = static_cast<uint8_t>(bs.byte);
+            }
+          }
+        }
+        if (out_col) {
+          // 16x1 blocks along the rows (tokens), one per column, after the
+          // Hadamard transform on the RHT path; two columns at a time
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float c0[16], c1[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              c0[i] = cur.get(i, 2 * k);
+              c1[i] = cur.get(i, 2 * k + 1);
+            }
+            if constexpr (kMode == kModeRHT) {
+              rht16(c0, p.sign_mask);
+              rht16(c1, p.sign_mask);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int j = 2 * k + h;
+              const uint64_t e0 = static_cast<uint64_t>(t.c0 + j) * static_cast<uint64_t>(rows) +
+                                  static_cast<uint64_t>(t.r0);
+              uint32_t w0, w1, sb;
+              column_block<kSR>(h == 0 ? c0 : c1, six_s, s, p.k0, p.k1, e0, p.offset, w0, w1, sb);
+              uint32_t* dst = reinterpret_cast<uint32_t*>(st.codes + (c_local0 + j) * kLdsCodeStride +
+                                                          (r_local >> 1));
+              dst[0] = w0;
+              dst[1] = w1;
+              st.col_scales[(c_local0 + j) * 16 + (r_local >> 4)] = static_cast<uint8_t>(sb);
             }
           }
         }
       }
-      if (out_col) {
-        // 16x1 blocks along the rows (tokens), one per column
+    }
+
+    if (!out_col && !stage_row_scales) return;
+    __syncthreads();
+    const int tid = threadIdx.x;
+    const int64_t tr = t.tr, tc = t.tc;
+    if (stage_row_scales) {
+      // one row's 8 scale bytes of this tile per thread
+      const int64_t row = tr * kTileRows + tid;
+      const int64_t nblk = (cols - tc * kTileCols) < kTileCols ? (cols - tc * kTileCols) >> 4 : 8;
+      if (row < rows) {
+        uint8_t* dst = p.s_row + row * (cols >> 4) + tc * 8;
+        if (nblk == 8 && ((cols >> 4) & 7) == 0) {
+          *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(st.row_scales + tid * 8);
+        } else {
+          for (int b = 0; b < nblk; ++b) dst[b] = st.row_scales[tid * 8 + b];
+        }
+      }
+    }
+    if (out_col) {
+      // each column's codes for this tile's rows are contiguous in q_col; 16
+      // lanes write one column's 128 bytes, and its 16 scale bytes (1D) leave
+      // as one store where alignment allows
+      const int64_t rows_here = (rows - tr * kTileRows) < kTileRows ? (rows - tr * kTileRows) : kTileRows;
+      const int code_chunks = static_cast<int>(rows_here >> 4);  // 8-byte chunks per column
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float col[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) col[i] = v[i][j];
-          const uint64_t e0 = static_cast<uint64_t>(t.c0 + j) * static_cast<uint64_t>(rows) +
-                              static_cast<uint64_t>(t.r0);
-          uint32_t w0, w1, sb;
-          column_block<kSR>(col, six_s, s, p.k0, p.k1, e0, p.offset, w0, w1, sb);
-          uint32_t* dst = reinterpret_cast<uint32_t*>(lds_codes + (c_local0 + j) * kLdsCodeStride +
-                                                      (r_local >> 1));
-          dst[0] = w0;
-          dst[1] = w1;
-          lds_scales[(c_local0 + j) * kLdsScaleStride + (r_local >> 4)] = static_cast<uint8_t>(sb);
+      for (int k = tid; k < kTileCols * (kTileRows / 16); k += kThreads) {
+        const int c_local = k >> 4, ch = k & 15;
+        const int64_t col = tc * kTileCols + c_local;
+        if (col < cols && ch < code_chunks) {
+          const uint2 val = *reinterpret_cast<const uint2*>(st.codes + c_local * kLdsCodeStride + ch * 8);
+          *reinterpret_cast<uint2*>(p.q_col + col * (rows >> 1) + tr * (kTileRows / 2) + ch * 8) = val;
+        }
+      }
+      if constexpr (kMode != kMode2D) {
+        if (tid < kTileCols) {
+          const int64_t col = tc * kTileCols + tid;
+          if (col < cols) {
+            uint8_t* dst = p.s_col + col * (rows >> 4) + tr * (kTileRows / 16);
+            if (code_chunks == 16 && ((rows >> 4) & 15) == 0) {
+              *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(st.col_scales + tid * 16);
+            } else {
+              for (int b = 0; b < code_chunks; ++b) dst[b] = st.col_scales[tid * 16 + b];
+            }
+          }
         }
       }
     }
   }
-
-  if (!out_col) return;
-  __syncthreads();
-  // Column-blocked copy: each column's codes for this tile's rows are
-  // contiguous in q_col; 16 lanes write one column's 128 bytes.
-  const int64_t rows_here = (rows - t.tr * kTileRows) < kTileRows ? (rows - t.tr * kTileRows)
-                                                                   : kTileRows;
-  const int code_chunks = static_cast<int>(rows_here >> 4);  // 8-byte chunks per column
-  for (int k = threadIdx.x; k < kTileCols * (kTileRows / 16); k += kThreads) {
-    const int c_local = k >> 4, ch = k & 15;
-    const int64_t col = t.tc * kTileCols + c_local;
-    if (col < cols && ch < code_chunks) {
-      const uint2 val = *reinterpret_cast<const uint2*>(lds_codes + c_local * kLdsCodeStride + ch * 8);
-      *reinterpret_cast<uint2*>(p.q_col + col * (rows >> 1) + t.tr * (kTileRows / 2) + ch * 8) = val;
-      if constexpr (kMode != kMode2D) {
-        p.s_col[col * (rows >> 4) + t.tr * (kTileRows / 16) + ch] =
-            lds_scales[c_local * kLdsScaleStride + ch];
-      }
-    }
-  }
-}
-
-template <typename InT>
-int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
-                uint32_t sign_mask, float* amax_ws, hipStream_t stream) {
-  fill_f32_kernel<<<1, 64, 0, stream>>>(amax_ws, 0.0f);
-  const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
-  const unsigned g = static_cast<unsigned>(tiles);
-  const bool ragged = (rows % 16) != 0;
-  if (rht) {
-    amax_kernel<InT, true, false><<<g, kThreads, 0, stream>>>(x, rows, cols, ldx, sign_mask, amax_ws);
-  } else if (ragged) {
-    amax_kernel<InT, false, true><<<g, kThreads, 0, stream>>>(x, rows, cols, ldx, sign_mask, amax_ws);
-  } else {
-    amax_kernel<InT, false, false><<<g, kThreads, 0, stream>>>(x, rows, cols, ldx, sign_mask, amax_ws);
-  }
-  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <typename InT, int kMode, bool kSR, bool kRagged>
@@ -398,6 +666,38 @@ void launch_quant(const QuantParams& p, hipStream_t stream) {
   const int64_t tiles =
       ((p.rows + kTileRows - 1) / kTileRows) * ((p.cols + kTileCols - 1) / kTileCols);
   quantize_kernel<InT, kMode, kSR, kRagged><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(p);
+}
+
+// Launches the amax kernel for x; returns the number of partial maxima it
+// writes (from ws + kPartialsOffset on), or -1 on a launch error.
+template <typename InT>
+int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
+                uint32_t sign_mask, float* amax_ws, hipStream_t stream) {
+  uint32_t* partials = reinterpret_cast<uint32_t*>(amax_ws) + kPartialsOffset;
+  int64_t g;
+  if (!rht && ldx == cols) {
+    const int64_t n = rows * cols;
+    const int64_t per_block = static_cast<int64_t>(kThreads) * kFlatUnroll * (16 / sizeof(InT));
+    g = (n + per_block - 1) / per_block;
+    if (g > kMaxPartials) g = kMaxPartials;
+    amax_flat_kernel<InT><<<static_cast<unsigned>(g), kThreads, 0, stream>>>(x, n, partials);
+  } else {
+    const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
+    g = tiles < kMaxTileBlocks ? tiles : kMaxTileBlocks;
+    const unsigned gg = static_cast<unsigned>(g);
+    const bool ragged = (rows % 16) != 0;
+    if (rht) {
+      amax_tile_kernel<InT, true, false><<<gg, kThreads, 0, stream>>>(x, rows, cols, ldx, sign_mask,
+                                                                       tiles, partials);
+    } else if (ragged) {
+      amax_tile_kernel<InT, false, true><<<gg, kThreads, 0, stream>>>(x, rows, cols, ldx, sign_mask,
+                                                                       tiles, partials);
+    } else {
+      amax_tile_kernel<InT, false, false><<<gg, kThreads, 0, stream>>>(x, rows, cols, ldx, sign_mask,
+                                                                        tiles, partials);
+    }
+  }
+  return hipGetLastError() == hipSuccess ? static_cast<int>(g) : -1;
 }
 
 // Ragged row counts (rows % 16 != 0) only reach the 1x16 row-only path: the
@@ -456,21 +756,25 @@ int launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
     empty_tensor_kernel<<<1, 64, 0, stream>>>(q.amax_in, q.amax_ws, q.tensor_scale, q.dev_status);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  const float* amax = q.amax_in;
-  if (amax == nullptr) {
-    const int rc = bf16 ? launch_amax(static_cast<const uint16_t*>(q.x), q.rows, q.cols, q.ldx,
-                                      q.rht, q.sign_mask, q.amax_ws, stream)
-                        : launch_amax(static_cast<const float*>(q.x), q.rows, q.cols, q.ldx,
-                                      q.rht, q.sign_mask, q.amax_ws, stream);
-    if (rc != 0) return rc;
-    amax = q.amax_ws;
-  }
   QuantParams p;
+  p.amax_in = q.amax_in;
+  p.partials = nullptr;
+  p.n_partials = 0;
+  p.amax_out = nullptr;
+  if (q.amax_in == nullptr) {
+    const int n = bf16 ? launch_amax(static_cast<const uint16_t*>(q.x), q.rows, q.cols, q.ldx,
+                                     q.rht, q.sign_mask, q.amax_ws, stream)
+                       : launch_amax(static_cast<const float*>(q.x), q.rows, q.cols, q.ldx,
+                                     q.rht, q.sign_mask, q.amax_ws, stream);
+    if (n < 0) return -1;
+    p.partials = reinterpret_cast<const uint32_t*>(q.amax_ws) + kPartialsOffset;
+    p.n_partials = n;
+    p.amax_out = q.amax_ws;
+  }
   p.x = q.x;
   p.rows = q.rows;
   p.cols = q.cols;
   p.ldx = q.ldx;
-  p.amax = amax;
   p.tensor_scale = q.tensor_scale;
   p.dev_status = q.dev_status;
   p.q_row = q.q_row;

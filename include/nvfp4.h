@@ -84,6 +84,13 @@ enum { NVFP4_ROUND_RN = 0, NVFP4_ROUND_SR = 1 };
 /* Output orientations (bit mask). */
 enum { NVFP4_OUT_ROW = 1, NVFP4_OUT_COL = 2 };
 
+/* Size of the amax workspace (amax_ws) of nvfp4_quantize and
+ * nvfp4_rht_quantize. Its first float receives the tensor amax; the rest
+ * holds per-workgroup partial maxima between the two kernels of a call and
+ * needs no initial value. The library cannot check the size of a plain
+ * pointer: a smaller buffer is written out of bounds. */
+#define NVFP4_AMAX_WS_BYTES 16384
+
 /*
  * nvfp4_quantize -- two-level NVFP4 quantization of an R x C matrix.
  * (gist.science summary, Resumen técnico §2 "Formato NVFP4"; for 16x16 blocks
@@ -92,7 +99,7 @@ enum { NVFP4_OUT_ROW = 1, NVFP4_OUT_COL = 2 };
  *   x          [rows][ldx] input, x_dtype NVFP4_F32 or NVFP4_BF16.
  *   rows, cols  >= 0. cols % 16 == 0. rows % 16 == 0 when NVFP4_OUT_COL is
  *               requested or block == NVFP4_BLOCK_2D. rows == 0 or cols == 0
- *               is an empty tensor: only *tensor_scale (= 1) and *amax_ws
+ *               is an empty tensor: only *tensor_scale (= 1) and amax_ws[0]
  *               (= 0) are written.
  *   ldx         >= cols.
  *   block       NVFP4_BLOCK_1D: row copy in 1x16 blocks along cols, column
@@ -106,8 +113,8 @@ enum { NVFP4_OUT_ROW = 1, NVFP4_OUT_COL = 2 };
  *               produced from one read of x and share the tensor scale.
  *   amax_in     NULL, or 1 float: the tensor amax to use instead of
  *               computing it (e.g. from an earlier pass).
- *   amax_ws     1 float of workspace, required when amax_in is NULL; holds
- *               the computed amax afterwards.
+ *   amax_ws     NVFP4_AMAX_WS_BYTES of workspace, required when amax_in is
+ *               NULL; amax_ws[0] holds the computed amax afterwards.
  *   q_row, s_row  row copy codes [rows][cols/2] and scales [rows][cols/16]
  *               (1D) or grid [rows/16][cols/16] (2D); required with OUT_ROW.
  *   q_col, s_col  column copy codes [cols][rows/2] and scales [cols][rows/16]
@@ -135,8 +142,9 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
  *              of one weight-gradient GEMM).
  *   rounding, seed, offset  as nvfp4_quantize (stream word 1).
  *   amax_in    NULL or 1 float: amax of the transformed tensor.
- *   amax_ws    1 float, required when amax_in is NULL (holds the amax of the
- *              transformed tensor afterwards).
+ *   amax_ws    NVFP4_AMAX_WS_BYTES of workspace, required when amax_in is
+ *              NULL (amax_ws[0] holds the amax of the transformed tensor
+ *              afterwards).
  *   q_t        codes [cols][tokens/2]; s_t scales [cols][tokens/16].
  *   tensor_scale, dev_status  as nvfp4_quantize.
  */

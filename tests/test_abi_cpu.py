@@ -146,3 +146,20 @@ def test_hook_argument_errors(L):
     assert L.nvfp4_philox_fill(1, 0, 0, 0, None, None) == 0
     assert L.nvfp4_rht_transform(FAKE, 1, 24, 32, 32, 7, FAKE, None) == 2
     assert L.nvfp4_rht_transform(FAKE, 1, 32, 32, 32, 7, None, None) == 1
+
+
+def test_amax_workspace_size_matches_header():
+    """The binding's workspace size is the header's, and it refuses smaller
+    buffers (the library cannot check a plain pointer)."""
+    import re
+
+    import torch
+
+    from bit_block_scaled_bf16_amd import _lib
+
+    text = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
+    m = re.search(r"#define NVFP4_AMAX_WS_BYTES (\d+)", text)
+    assert m is not None and int(m.group(1)) == _lib.AMAX_WS_BYTES
+    with pytest.raises(ValueError):
+        _lib._ws(torch.zeros(4, dtype=torch.float32))
+    assert _lib._ws(torch.zeros(_lib.AMAX_WS_BYTES // 4, dtype=torch.float32)) is not None
