@@ -40,7 +40,23 @@ TOKENS, HIDDEN, FFN = 16384, 5120, 20480
 # HBM traffic per GEMM launch comes from the committed counter summary below
 # (null when it is missing or the GEMM source changed since it was taken).
 TRAFFIC_SUMMARY = "linear_layer_traffic.md"
-GEMM_KERNEL_NAMES = {"gemm_fprop": "gemm_kernel<false, true,", "gemm_wgrad": "gemm_kernel<false, false,"}
+# Kernels of each call, as (short-name fragment, dispatch index within one
+# step) in the counter summary: a quantize call is an amax kernel and a
+# quantize kernel; a GEMM call launches 256 x 256 tiles and, for a last
+# partial round, 128 x 128 ones.
+CALL_KERNELS = {
+    "quantize_x_1x16": (("amax_flat_kernel<unsigned short>", 0),
+                        ("quantize_kernel<unsigned short, 0, false, false>", 0)),
+    "quantize_w_16x16": (("amax_flat_kernel<unsigned short>", 1),
+                         ("quantize_kernel<unsigned short, 1, false, false>", 0)),
+    "rht_quantize_dy_sr": (("amax_tile_kernel<unsigned short, true, false>", 0),
+                           ("quantize_kernel<unsigned short, 2, true, false>", 0)),
+    "rht_quantize_x_rn": (("amax_tile_kernel<unsigned short, true, false>", 1),
+                          ("quantize_kernel<unsigned short, 2, false, false>", 0)),
+    "gemm_fprop": (("gemm_kernel<4, false, true,", 0), ("gemm_kernel<2, false, true,", 0)),
+    "gemm_wgrad": (("gemm_kernel<4, false, false,", 0), ("gemm_kernel<2, false, false,", 0)),
+}
+CALL_SOURCE = {n: ("gemm_kernel" if n.startswith("gemm") else "quantize_kernel") for n in CALL_KERNELS}
 
 
 def parse():
@@ -121,8 +137,8 @@ class Step:
 
 
 def cpu_baseline():
-    """The oracle on a bounded slice of the step: 512 tokens, the first 2048
-    rows of W; same operations and seeds. Returns its effective TFLOP/s."""
+    """The oracle on a bounded slice of the step: 4096 tokens, the first
+    10240 rows of W; same operations and seeds. Returns its effective TFLOP/s."""
     import numpy as np
 
     import oracle as o
@@ -134,7 +150,7 @@ def cpu_baseline():
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         blas_threads = 1
-    t, h, f = 2048, HIDDEN, 10240
+    t, h, f = 4096, HIDDEN, 10240
     x = wl.normal((t, h), seed=5, outlier_channels=16)
     w = wl.weight(f, h, seed=2)
     dy = wl.laplace((t, f), seed=6)
@@ -166,8 +182,9 @@ def cpu_baseline():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the data-parallel "
-              "path shards by tokens, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: a data-parallel "
+              "run would shard the tokens and reduce the weight gradient across GPUs, which this "
+              "library does not do", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -212,6 +229,9 @@ def main():
 
     ms_step = elapsed * 1e3 / args.steps
     work = step.work()
+    from bit_block_scaled_bf16_amd import profiling
+
+    summary = os.path.join(ROOT, "profiles", TRAFFIC_SUMMARY)
     kernels = {}
     for i, (name, _) in enumerate(calls):
         ms = [events[k][i][0].elapsed_time(events[k][i][1]) for k in range(args.steps)]
@@ -224,7 +244,9 @@ def main():
             rate = amount / (avg_ms * 1e-3) / 1e12
             peak = MFMA_PEAK_TFLOPS
         kernels[name] = {"us": round(avg_ms * 1e3, 2), "achieved": round(rate, 1), "unit": unit,
-                         "frac": round(rate / peak, 4), "work": amount}
+                         "frac": round(rate / peak, 4), "work": amount,
+                         "traffic": profiling.kernel_traffic(summary, CALL_KERNELS[name],
+                                                             CALL_SOURCE[name])}
 
     gemm_flops = work["gemm_fprop"][1] + work["gemm_wgrad"][1]
     value = gemm_flops / (ms_step * 1e-3) / 1e12
@@ -233,10 +255,7 @@ def main():
     q_us = sum(kernels[n]["us"] for n in q_names)
     g_us = kernels["gemm_fprop"]["us"] + kernels["gemm_wgrad"]["us"]
     dom = max(("gemm_fprop", "gemm_wgrad"), key=lambda n: kernels[n]["us"])
-    from bit_block_scaled_bf16_amd import profiling
-
-    traffic = profiling.kernel_traffic(
-        os.path.join(ROOT, "profiles", TRAFFIC_SUMMARY), GEMM_KERNEL_NAMES[dom], "gemm_kernel")
+    traffic = kernels[dom]["traffic"]
     roofline = {
         "bound": "mfma",
         "kernel": dom,

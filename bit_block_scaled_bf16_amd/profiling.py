@@ -39,7 +39,8 @@ CALIBRATION_KERNEL = "bitwise_not"
 KERNEL_SOURCES = {
     "gemm_kernel": "gemm.hip",
     "quantize_kernel": "quantize.hip",
-    "amax_kernel": "quantize.hip",
+    "amax_flat_kernel": "quantize.hip",
+    "amax_tile_kernel": "quantize.hip",
 }
 
 
@@ -162,20 +163,26 @@ def load_traffic(md_path: str):
     return json.loads(m.group(1)) if m else None
 
 
-def kernel_traffic(md_path: str, name_fragment: str, source_key: str, dispatch_index: int = 0):
-    """HBM bytes (read + write) of one dispatch of the kernel whose short name
-    contains name_fragment, or None when the summary is missing or the
-    kernel's source changed since it was taken."""
+def kernel_traffic(md_path: str, kernels, source_key: str):
+    """HBM bytes (read + write) of one call: the sum over `kernels`, a list of
+    (short-name fragment, dispatch index) pairs, of that dispatch of the
+    first kernel whose short name contains the fragment. None when the
+    summary is missing, none of the kernels is in it, or the source of
+    source_key changed since it was taken."""
     data = load_traffic(md_path)
     if data is None:
         return None
     src = KERNEL_SOURCES.get(source_key)
     if src is None or data["sources"].get(source_key) != source_hash(src):
         return None
-    for name, d in data["kernels"].items():
-        if name_fragment in name and dispatch_index < d["dispatches"]:
-            return d["fetch_bytes"][dispatch_index] + d["write_bytes"][dispatch_index]
-    return None
+    total, found = 0, False
+    for frag, idx in kernels:
+        for name, d in data["kernels"].items():
+            if frag in name and idx < d["dispatches"]:
+                total += d["fetch_bytes"][idx] + d["write_bytes"][idx]
+                found = True
+                break
+    return total if found else None
 
 
 if __name__ == "__main__":
