@@ -92,25 +92,24 @@ __device__ __forceinline__ uint32_t pack8_rn(const float* y) {
 
 // Stochastically rounded E2M1 code of y from 16 random bits u16: with
 // a = min(|y|, 6), lo the largest magnitude <= a and hi the next one, round
-// up exactly when u16 / 2^16 < (a - lo) / (hi - lo).
+// up exactly when (a - lo) / (hi - lo) + u16 / 2^16 >= 1.
 //
-// One branch-free formula covers every magnitude: with e' = max(exponent of
-// a, 0) (0 below 2, 1 in [2, 4), 2 in [4, 6]), v = a * 2^(1 - e') lies in
-// [0, 4) and the E2M1 grid around a maps to the integers around v, so
-// lo's code is floor(v) + 2 e' and the fraction is v - floor(v). Scaling by a
-// power of two, floor and the subtraction are exact in float32, so the
-// comparison with u16 / 2^16 is exact too.
+// Scaled by 2^-126, the E2M1 grid is float32's own bit layout: 1.0 is the
+// smallest normal, the magnitudes below 1 fall in the subnormal range with
+// its uniform spacing, and each binade above holds two grid points, like one
+// mantissa bit. So with B = a's bits on that scale, B >> 22 is lo's code and
+// the 22 bits below are frac * 2^22, and adding u16 * 2^6 carries into bit
+// 22 exactly when frac + u16 / 2^16 >= 1. For a >= 1, B is a's own bits
+// with the exponent lowered by 126 (exact). For a < 1, B = floor(a * 2^23):
+// the floor drops only bits below 2^-22 of a step, and since u16 * 2^6 is an
+// integer, floor((B + u16 * 2^6) / 2^22) still equals floor(2a + u16 / 2^16).
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
   const uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
   const float a = fminf(fabsf(y), 6.0f);
-  const int e = static_cast<int>(__float_as_uint(a) >> 23) - 127;
-  const int ep = e > 0 ? e : 0;
-  const float v = a * __uint_as_float(static_cast<uint32_t>(128 - ep) << 23);  // a * 2^(1 - e')
-  const float fl = __builtin_floorf(v);
-  const float frac = v - fl;
-  const uint32_t code = static_cast<uint32_t>(fl) + 2u * static_cast<uint32_t>(ep) +
-                        ((static_cast<float>(u16) < frac * 65536.0f) ? 1u : 0u);
-  return code | sign;
+  const uint32_t b_norm = __float_as_uint(a) - (126u << 23);
+  const uint32_t b_sub = static_cast<uint32_t>(__fmul_rn(a, 8388608.0f));  // floor(a * 2^23)
+  const uint32_t b = (a < 1.0f) ? b_sub : b_norm;
+  return ((b + (u16 << 6)) >> 22) | sign;
 }
 
 // ---------------------------------------------------------------------------
@@ -133,7 +132,9 @@ __device__ __forceinline__ U4 philox4x32_10(uint32_t k0, uint32_t k1, U4 c) {
     const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c.z;
     const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
     const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
-    c = U4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    // three-way xors as one gfx950 v_bitop3_b32 each (truth table 0x96)
+    c = U4{static_cast<uint32_t>(__builtin_amdgcn_bitop3_b32(hi1, c.y, k0, 0x96)), lo1,
+           static_cast<uint32_t>(__builtin_amdgcn_bitop3_b32(hi0, c.w, k1, 0x96)), lo0};
     k0 += kPhiloxW0;
     k1 += kPhiloxW1;
   }
@@ -180,13 +181,32 @@ __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v
 // mapping (a, b) -> (a + b, a - b), then a multiply by 1/4 (exact).
 // sign_mask bit i set means the input i is negated first.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
+
+// The signs as +-1.0 floats (the same for every column of a launch).
+struct RhtSigns {
+  float d[16];
+};
+
+__device__ __forceinline__ RhtSigns rht_signs(uint32_t sign_mask) {
+  RhtSigns g;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((sign_mask >> i) & 1u) << 31));
+  for (int i = 0; i < 16; ++i) g.d[i] = ((sign_mask >> i) & 1u) ? -1.0f : 1.0f;
+  return g;
+}
+
+// The transform without the final 1/4. The signs ride on the first stage:
+// t = d_b * b is exact and fma(d_a, a, +-t) rounds d_a a +- d_b b once, as
+// the add of the negated values does.
+__device__ __forceinline__ void rht16_unscaled(float* v, const RhtSigns& g) {
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const float t = __fmul_rn(g.d[i + 1], v[i + 1]);
+    const float a = v[i];
+    v[i] = __builtin_fmaf(g.d[i], a, t);
+    v[i + 1] = __builtin_fmaf(g.d[i], a, -t);
   }
 #pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
+  for (int h = 2; h < 16; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if ((i & h) == 0) {
@@ -196,6 +216,10 @@ __device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
       }
     }
   }
+}
+
+__device__ __forceinline__ void rht16(float* v, const RhtSigns& g) {
+  rht16_unscaled(v, g);
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = __fmul_rn(v[i], 0.25f);
 }

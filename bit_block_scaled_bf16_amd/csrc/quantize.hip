@@ -132,12 +132,13 @@ __device__ __forceinline__ void load_sub_tile(const InT* __restrict__ x, int64_t
 
 // Applies the Hadamard transform to each of the 8 columns (16 tokens each).
 __device__ __forceinline__ void rht_columns(float (&v)[16][8], uint32_t sign_mask) {
+  const RhtSigns g = rht_signs(sign_mask);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float col[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) col[i] = v[i][j];
-    rht16(col, sign_mask);
+    rht16(col, g);
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i][j] = col[i];
   }
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* __restri
 // bytes are requested before the current one is transformed, and the
 // transform goes one pair of columns at a time (32 floats live).
 template <bool kRht>
-__device__ __forceinline__ uint32_t absmax_bf16_tile(const uint4 (&raw)[16], uint32_t sign_mask,
+__device__ __forceinline__ uint32_t absmax_bf16_tile(const uint4 (&raw)[16], const RhtSigns& g,
                                                      uint32_t m) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -255,8 +256,8 @@ __device__ __forceinline__ uint32_t absmax_bf16_tile(const uint4 (&raw)[16], uin
       c1[i] = bf16_hi(w);
     }
     if constexpr (kRht) {
-      rht16(c0, sign_mask);
-      rht16(c1, sign_mask);
+      rht16_unscaled(c0, g);
+      rht16_unscaled(c1, g);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -286,6 +287,7 @@ __global__ __launch_bounds__(kThreads) void amax_tile_kernel(const InT* __restri
                                                              uint32_t* __restrict__ partials) {
   __shared__ uint32_t lds4[kThreads / 64];
   uint32_t m = 0;
+  const RhtSigns g = rht_signs(sign_mask);
   if constexpr (sizeof(InT) == 2) {
     // invalid lanes (past the columns) load zeros, which leave the max alone
     int64_t tile = blockIdx.x;
@@ -297,8 +299,11 @@ __global__ __launch_bounds__(kThreads) void amax_tile_kernel(const InT* __restri
       for (int i = 0; i < 16; ++i) cur[i] = raw[i];
       const int64_t next = tile + gridDim.x;
       if (next < tiles) load_raw_bf16<kRagged>(x, ldx, locate_tile(next, rows, cols), raw);
-      m = absmax_bf16_tile<kRht>(cur, sign_mask, m);
+      m = absmax_bf16_tile<kRht>(cur, g, m);
     }
+    // the 1/4 of the transform, applied to the maximum: rounding is
+    // monotonic and symmetric, so max |RN(h / 4)| = RN(max |h| / 4)
+    if constexpr (kRht) m = __float_as_uint(__fmul_rn(__uint_as_float(m), 0.25f));
   } else {
     for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
       const Tile t = locate_tile(tile, rows, cols);
@@ -500,6 +505,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     if (p.amax_out != nullptr) *p.amax_out = amax;
     if (!(amax <= 3.402823466e38f) && p.dev_status != nullptr) *p.dev_status = 1;
   }
+  const RhtSigns g = rht_signs(p.sign_mask);
   const bool out_row = (p.outputs & 1) != 0 && kMode != kModeRHT;
   const bool out_col = (p.outputs & 2) != 0 || kMode == kModeRHT;
   const bool stage_row_scales = out_row && kMode != kMode2D;
@@ -591,8 +597,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
               c1[i] = cur.get(i, 2 * k + 1);
             }
             if constexpr (kMode == kModeRHT) {
-              rht16(c0, p.sign_mask);
-              rht16(c1, p.sign_mask);
+              rht16(c0, g);
+              rht16(c1, g);
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {

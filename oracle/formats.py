@@ -25,8 +25,10 @@ Readings (the pages fix none of these):
   saturating at 448 -- never NaN.
 * Stochastic rounding to E2M1: with ``a = min(|y|, 6)``, ``lo`` the largest
   magnitude <= a and ``hi`` the next one, round up to ``hi`` exactly when
-  ``u16 / 2^16 < (a - lo) / (hi - lo)``, with ``u16`` a uniform 16-bit random
-  integer. The pages only say that gradients are rounded at random so that the
+  ``(a - lo) / (hi - lo) + u16 / 2^16 >= 1``, with ``u16`` a uniform 16-bit
+  random integer: the random fraction is added below the grid step and the
+  sum is truncated, which rounds up with probability floor(frac * 2^16) /
+  2^16. The pages only say that gradients are rounded at random so that the
   rounding is unbiased (Resumen técnico §2, "Escalado Bidimensional (2D) y
   Redondeo Estocástico"; Lo esencial, item 4).
 """
@@ -101,8 +103,9 @@ def e2m1_encode_sr(y, u16) -> np.ndarray:
     hi = np.minimum(lo + 1, 7)
     step = mags[hi] - mags[lo]
     frac = np.where(step > 0, (a - mags[lo]) / np.where(step > 0, step, 1.0), 0.0)
-    u = u16.astype(np.float64) / 65536.0
-    mag_code = np.where(u < frac, hi, lo).astype(np.uint8)
+    # frac + u16 / 2^16 >= 1, compared exactly: frac * 2^16 is exact in
+    # float64 (a power-of-two scaling) and 2^16 - u16 is an integer
+    mag_code = np.where(frac * 65536.0 >= 65536 - u16, hi, lo).astype(np.uint8)
     sign = np.signbit(y).astype(np.uint8) << 3
     return (mag_code | sign).astype(np.uint8)
 

@@ -10,8 +10,8 @@
   the 16x16 weight codes of W^T are the transposed codes of W, so W and W^T
   dequantize to transposes of each other bit for bit.
 * Stochastic rounding: over all 2^16 random words, the number that round up is
-  exactly ceil(frac * 2^16); the mean of many SR draws equals the input
-  within a stated sigma bound.
+  exactly floor(frac * 2^16), and they are the largest words; the mean of
+  many SR draws equals the input within a stated sigma bound.
 * Memory: 0.5 + 1/16 bytes per element (4.5 bits), 1.78x smaller than FP8.
 """
 
@@ -174,7 +174,10 @@ def test_sr_counts_over_all_random_words(y):
     hi = min(lo + 1, 7)
     ups = int(np.sum(codes == hi)) if hi != lo else 0
     frac = 0.0 if hi == lo else (a - mags[lo]) / (mags[hi] - mags[lo])
-    assert ups == math.ceil(frac * 65536)
+    assert ups == math.floor(frac * 65536)
+    # the words that round up are the largest ones (u16 >= 2^16 (1 - frac))
+    if ups:
+        assert np.all(codes[65536 - ups:] == hi) and np.all(codes[:65536 - ups] == lo)
     assert np.all((codes == lo) | (codes == hi))
     # negative inputs mirror
     assert np.array_equal(o.e2m1_encode_sr(-yy, u), codes | 8)
