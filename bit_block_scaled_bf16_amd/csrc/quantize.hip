@@ -324,23 +324,25 @@ __global__ __launch_bounds__(kThreads) void amax_tile_kernel(const InT* __restri
 }
 
 // The tensor amax from n <= kMaxPartials partial maxima. Each wave reduces
-// them on its own (4 loads of 16 bytes per lane and a wave maximum: no LDS,
-// no barrier). Entries past n hold stale values and are masked off.
+// them on its own: 4 loads of 16 bytes per lane, all issued before the
+// first is needed (entries past n hold stale values and are masked off,
+// and the loads stay inside the workspace), then a wave maximum: no LDS, no
+// barrier.
 __device__ __forceinline__ float reduce_partials(const uint32_t* __restrict__ partials, int n) {
   const int lane = threadIdx.x & 63;
   const uint4* p4 = reinterpret_cast<const uint4*>(partials);
+  uint4 b[kMaxPartials / 256];
+#pragma unroll
+  for (int k = 0; k < kMaxPartials / 256; ++k) b[k] = p4[lane + 64 * k];
   uint32_t m = 0;
 #pragma unroll
   for (int k = 0; k < kMaxPartials / 256; ++k) {
     const int i = 4 * (lane + 64 * k);
-    if (i < n) {
-      const uint4 b = p4[lane + 64 * k];
-      const uint32_t v[4] = {b.x, b.y, b.z, b.w};
+    const uint32_t v[4] = {b[k].x, b[k].y, b[k].z, b[k].w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t x = i + c < n ? v[c] : 0u;
-        m = x > m ? x : m;
-      }
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t x = i + c < n ? v[c] : 0u;
+      m = x > m ? x : m;
     }
   }
   return __uint_as_float(wave_max_u32(m));
@@ -497,6 +499,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   __shared__ __attribute__((aligned(16))) Staging st;
 
   const int64_t rows = p.rows, cols = p.cols;
+  const Tile t = locate(rows, cols);
+  // the tile's loads go out first; the amax (a few more loads) is reduced
+  // while they are in flight
+  RawTile<InT> cur;
+  load_raw<InT, kRagged>(static_cast<const InT*>(p.x), p.ldx, t, cur);
   const float amax = p.amax_in != nullptr ? *p.amax_in : reduce_partials(p.partials, p.n_partials);
   const float s = tensor_scale_from_amax(amax);
   const float six_s = __fmul_rn(6.0f, s);
@@ -509,9 +516,6 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   const bool out_row = (p.outputs & 1) != 0 && kMode != kModeRHT;
   const bool out_col = (p.outputs & 2) != 0 || kMode == kModeRHT;
   const bool stage_row_scales = out_row && kMode != kMode2D;
-  const Tile t = locate(rows, cols);
-  RawTile<InT> cur;
-  load_raw<InT, kRagged>(static_cast<const InT*>(p.x), p.ldx, t, cur);
   {
     const int c_local0 = t.cg * 8;
     const int r_local = t.wave * 64 + t.rg * 16;
