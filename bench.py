@@ -55,6 +55,10 @@ CALL_KERNELS = {
                           ("quantize_kernel<unsigned short, 2, false, false>", 0)),
     "gemm_fprop": (("gemm_kernel<4, false, true,", 0), ("gemm_kernel<2, false, true,", 0)),
     "gemm_wgrad": (("gemm_kernel<4, false, false,", 0), ("gemm_kernel<2, false, false,", 0)),
+    # the dgrad path, run after the step
+    "quantize_dy_1x16_sr": (("amax_flat_kernel<unsigned short>", 2),
+                            ("quantize_kernel<unsigned short, 0, true, false>", 0)),
+    "gemm_dgrad": (("gemm_kernel<4, false, true,", 1), ("gemm_kernel<2, false, true,", 1)),
 }
 CALL_SOURCE = {n: ("gemm_kernel" if n.startswith("gemm") else "quantize_kernel") for n in CALL_KERNELS}
 
@@ -95,6 +99,9 @@ class Step:
         # RHT copies (wgrad operands), stored [cols][tokens/2]
         self.qdy, self.sdy, self.tdy, self.ady = e(f, t // 2), e(f, t // 16), sc(), ws()
         self.qxt, self.sxt, self.txt, self.axt = e(h, t // 2), e(h, t // 16), sc(), ws()
+        # dgrad: SR row copy of dY (A) and dX = dY W, whose B operand is W^T's copy
+        self.qdyr, self.sdyr, self.tdyr, self.adyr = e(t, f // 2), e(t, f // 16), sc(), ws()
+        self.dx = torch.empty((t, h), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((t, f), dtype=torch.bfloat16, device=dev)
         self.dw = torch.empty((f, h), dtype=torch.bfloat16, device=dev)
         self.status = torch.zeros(4, dtype=torch.int32, device=dev)
@@ -122,6 +129,20 @@ class Step:
                 s.t, s.dw)),
         ]
 
+    def next_calls(self):
+        """The dgrad path, timed apart from the step (it is not one of the
+        step's rows): the SR row copy of dY and dX = deq(Q_SR(dY)) deq(Q2D(W))."""
+        nv = self.nv
+        s = self
+        return [
+            ("quantize_dy_1x16_sr", lambda: nv.nvfp4_quantize(
+                s.dy, nv.BLOCK_1D, nv.ROUND_SR, 7, s.offset, nv.OUT_ROW, None, s.adyr, s.qdyr,
+                s.sdyr, None, None, s.tdyr, s.status)),
+            ("gemm_dgrad", lambda: nv.nvfp4_gemm(
+                s.qdyr, s.sdyr, s.tdyr, nv.BLOCK_1D, s.qwt, s.swt, s.tw, nv.BLOCK_2D, s.t, s.h,
+                s.f, s.dx)),
+        ]
+
     def work(self):
         """Algorithmic bytes (quantizer calls, amax pass included) or flops."""
         t, h, f = self.t, self.h, self.f
@@ -133,6 +154,8 @@ class Step:
             "rht_quantize_x_rn": ("GB/s", t * h * (2 + 2 + q1)),
             "gemm_fprop": ("TFLOP/s", 2.0 * t * f * h),
             "gemm_wgrad": ("TFLOP/s", 2.0 * f * h * t),
+            "quantize_dy_1x16_sr": ("GB/s", t * f * (2 + 2 + q1)),
+            "gemm_dgrad": ("TFLOP/s", 2.0 * t * h * f),
         }
 
 
@@ -227,26 +250,47 @@ def main():
     elapsed = time.perf_counter() - t0
     assert int(step.status.cpu()[0]) == 0, "non-finite amax"
 
+    # the dgrad path, after the timed step and outside it
+    next_calls = step.next_calls()
+    for _ in range(min(args.warmup, 1)):
+        for _, fn in next_calls:
+            fn()
+    next_events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in next_calls] for _ in range(args.steps)]
+    for k in range(args.steps):
+        for i, (_, fn) in enumerate(next_calls):
+            next_events[k][i][0].record()
+            fn()
+            next_events[k][i][1].record()
+    torch.cuda.synchronize()
+    assert int(step.status.cpu()[0]) == 0, "non-finite amax"
+
     ms_step = elapsed * 1e3 / args.steps
     work = step.work()
     from bit_block_scaled_bf16_amd import profiling
 
     summary = os.path.join(ROOT, "profiles", TRAFFIC_SUMMARY)
-    kernels = {}
-    for i, (name, _) in enumerate(calls):
-        ms = [events[k][i][0].elapsed_time(events[k][i][1]) for k in range(args.steps)]
-        avg_ms = float(np.mean(ms))
-        unit, amount = work[name]
-        if unit == "GB/s":
-            rate = amount / (avg_ms * 1e-3) / 1e9
-            peak = HBM_PEAK_GBS
-        else:
-            rate = amount / (avg_ms * 1e-3) / 1e12
-            peak = MFMA_PEAK_TFLOPS
-        kernels[name] = {"us": round(avg_ms * 1e3, 2), "achieved": round(rate, 1), "unit": unit,
+
+    def call_stats(call_list, evs):
+        res = {}
+        for i, (name, _) in enumerate(call_list):
+            ms = [evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)]
+            avg_ms = float(np.mean(ms))
+            unit, amount = work[name]
+            if unit == "GB/s":
+                rate = amount / (avg_ms * 1e-3) / 1e9
+                peak = HBM_PEAK_GBS
+            else:
+                rate = amount / (avg_ms * 1e-3) / 1e12
+                peak = MFMA_PEAK_TFLOPS
+            res[name] = {"us": round(avg_ms * 1e3, 2), "achieved": round(rate, 1), "unit": unit,
                          "frac": round(rate / peak, 4), "work": amount,
                          "traffic": profiling.kernel_traffic(summary, CALL_KERNELS[name],
                                                              CALL_SOURCE[name])}
+        return res
+
+    kernels = call_stats(calls, events)
+    next_rows = call_stats(next_calls, next_events)
 
     gemm_flops = work["gemm_fprop"][1] + work["gemm_wgrad"][1]
     value = gemm_flops / (ms_step * 1e-3) / 1e12
@@ -291,6 +335,7 @@ def main():
                  "frac": round(gemm_flops / (g_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4),
                  "us": round(g_us, 1)},
         "kernels": kernels,
+        "next": {"dgrad": next_rows},
         "roofline": roofline,
         "cpu_baseline": None,
     }
