@@ -31,7 +31,7 @@ def host(t) -> np.ndarray:
     import torch
 
     torch.cuda.synchronize()
-    return t.cpu().numpy()
+    return t.detach().cpu().numpy()
 
 
 def e2m1_step_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:

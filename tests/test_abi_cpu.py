@@ -163,3 +163,18 @@ def test_amax_workspace_size_matches_header():
     with pytest.raises(ValueError):
         _lib._ws(torch.zeros(4, dtype=torch.float32))
     assert _lib._ws(torch.zeros(_lib.AMAX_WS_BYTES // 4, dtype=torch.float32)) is not None
+
+
+def test_nvfp4_linear_refuses_cpu_tensors_and_opts_out_to_bf16():
+    """The NVFP4 layer has no CPU path (it raises); the bf16 opt-out is a
+    plain matmul and runs anywhere."""
+    import torch
+
+    from bit_block_scaled_bf16_amd.linear import NVFP4Linear
+
+    x = torch.randn(32, 64).to(torch.bfloat16)
+    layer = NVFP4Linear(64, 16)
+    with pytest.raises(RuntimeError):
+        layer(x)
+    off = NVFP4Linear(64, 16, nvfp4=False)
+    assert torch.equal(off(x), x @ off.weight.t())
