@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the dgrad calls timed after the step (they share the fprop GEMM's "
+                         "kernel, whose per-kernel profile statistics would then mix both)")
     ap.add_argument("--tokens", type=int, default=TOKENS)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one copy-like kernel (torch.bitwise_not on int32) "
@@ -251,7 +254,7 @@ def main():
     assert int(step.status.cpu()[0]) == 0, "non-finite amax"
 
     # the dgrad path, after the timed step and outside it
-    next_calls = step.next_calls()
+    next_calls = [] if args.no_next else step.next_calls()
     for _ in range(min(args.warmup, 1)):
         for _, fn in next_calls:
             fn()
@@ -335,7 +338,7 @@ def main():
                  "frac": round(gemm_flops / (g_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4),
                  "us": round(g_us, 1)},
         "kernels": kernels,
-        "next": {"dgrad": next_rows},
+        "next": {"dgrad": next_rows} if next_rows else None,
         "roofline": roofline,
         "cpu_baseline": None,
     }
