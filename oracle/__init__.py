@@ -42,6 +42,9 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
                          SR unbiasedness.
 * gemm.*              -- pinned: pure-Python triple loop on tiny inputs,
                          all-ones closed form, unit-row selection.
+* mx.*                -- pinned: E8M0 bytes against float32 exponent fields,
+                         the [4, 8) scale invariant, a hand-worked block,
+                         power-of-two invariance, a triple loop for the GEMM.
 """
 
 from .formats import (
@@ -52,6 +55,7 @@ from .formats import (
     e4m3_decode,
     e4m3_encode,
 )
+from .mx import MX_BLOCK, e8m0_decode, mx_dequantize, mx_gemm, mx_quantize, mx_scale_bytes
 from .philox import philox4x32_10, sr_random_u16
 from .hadamard import hadamard16, rht_signs, rht
 from .quantize import (
@@ -68,6 +72,12 @@ from .quantize import (
 from .gemm import gemm
 
 __all__ = [
+    "MX_BLOCK",
+    "e8m0_decode",
+    "mx_dequantize",
+    "mx_gemm",
+    "mx_quantize",
+    "mx_scale_bytes",
     "E2M1_MAGNITUDES",
     "e2m1_decode",
     "e2m1_encode_rn",
