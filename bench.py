@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 METRIC = "NVFP4 quantize GB/s (% HBM peak) + NVFP4 GEMM TFLOP/s (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 MFMA, MI355X
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # dense FP4 MFMA (the MXFP4 comparison GEMM), MI355X
 
 TOKENS, HIDDEN, FFN = 16384, 5120, 20480
 
@@ -59,8 +60,12 @@ CALL_KERNELS = {
     "quantize_dy_1x16_sr": (("amax_flat_kernel<unsigned short>", 2),
                             ("quantize_kernel<unsigned short, 0, true, false>", 0)),
     "gemm_dgrad": (("gemm_kernel<4, false, true,", 1), ("gemm_kernel<2, false, true,", 1)),
+    "mx_quantize_x": (("mx_quantize_kernel<unsigned short>", 0),),
+    "mx_quantize_w": (("mx_quantize_kernel<unsigned short>", 1),),
+    "mx_gemm_fprop": (("mx_gemm_kernel<true>", 0),),
 }
-CALL_SOURCE = {n: ("gemm_kernel" if n.startswith("gemm") else "quantize_kernel") for n in CALL_KERNELS}
+CALL_SOURCE = {n: ("mxfp4" if n.startswith("mx_") else
+                   "gemm_kernel" if n.startswith("gemm") else "quantize_kernel") for n in CALL_KERNELS}
 
 
 def parse():
@@ -105,6 +110,9 @@ class Step:
         # dgrad: SR row copy of dY (A) and dX = dY W, whose B operand is W^T's copy
         self.qdyr, self.sdyr, self.tdyr, self.adyr = e(t, f // 2), e(t, f // 16), sc(), ws()
         self.dx = torch.empty((t, h), dtype=torch.bfloat16, device=dev)
+        # MXFP4 comparison: X and W in 1x32 blocks, fprop on the FP4 MFMA
+        self.mqx, self.msx = e(t, h // 2), e(t, h // 32)
+        self.mqw, self.msw = e(f, h // 2), e(f, h // 32)
         self.y = torch.empty((t, f), dtype=torch.bfloat16, device=dev)
         self.dw = torch.empty((f, h), dtype=torch.bfloat16, device=dev)
         self.status = torch.zeros(4, dtype=torch.int32, device=dev)
@@ -146,6 +154,17 @@ class Step:
                 s.f, s.dx)),
         ]
 
+    def mx_calls(self):
+        """The MXFP4 comparison path, timed apart from the step."""
+        nv = self.nv
+        s = self
+        return [
+            ("mx_quantize_x", lambda: nv.mxfp4_quantize(s.x, s.mqx, s.msx)),
+            ("mx_quantize_w", lambda: nv.mxfp4_quantize(s.w, s.mqw, s.msw)),
+            ("mx_gemm_fprop", lambda: nv.mxfp4_gemm(s.mqx, s.msx, s.mqw, s.msw, s.t, s.f, s.h,
+                                                    s.y)),
+        ]
+
     def work(self):
         """Algorithmic bytes (quantizer calls, amax pass included) or flops."""
         t, h, f = self.t, self.h, self.f
@@ -159,6 +178,10 @@ class Step:
             "gemm_wgrad": ("TFLOP/s", 2.0 * f * h * t),
             "quantize_dy_1x16_sr": ("GB/s", t * f * (2 + 2 + q1)),
             "gemm_dgrad": ("TFLOP/s", 2.0 * t * h * f),
+            # MXFP4: one pass (no tensor amax): bf16 in, codes + 1/32 scale bytes out
+            "mx_quantize_x": ("GB/s", t * h * (2 + 0.5 + 1.0 / 32)),
+            "mx_quantize_w": ("GB/s", f * h * (2 + 0.5 + 1.0 / 32)),
+            "mx_gemm_fprop": ("FP4 TFLOP/s", 2.0 * t * f * h),
         }
 
 
@@ -254,7 +277,7 @@ def main():
     assert int(step.status.cpu()[0]) == 0, "non-finite amax"
 
     # the dgrad path, after the timed step and outside it
-    next_calls = [] if args.no_next else step.next_calls()
+    next_calls = [] if args.no_next else step.next_calls() + step.mx_calls()
     for _ in range(min(args.warmup, 1)):
         for _, fn in next_calls:
             fn()
@@ -285,7 +308,7 @@ def main():
                 peak = HBM_PEAK_GBS
             else:
                 rate = amount / (avg_ms * 1e-3) / 1e12
-                peak = MFMA_PEAK_TFLOPS
+                peak = FP4_MFMA_PEAK_TFLOPS if unit.startswith("FP4") else MFMA_PEAK_TFLOPS
             res[name] = {"us": round(avg_ms * 1e3, 2), "achieved": round(rate, 1), "unit": unit,
                          "frac": round(rate / peak, 4), "work": amount,
                          "traffic": profiling.kernel_traffic(summary, CALL_KERNELS[name],
@@ -338,7 +361,9 @@ def main():
                  "frac": round(gemm_flops / (g_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4),
                  "us": round(g_us, 1)},
         "kernels": kernels,
-        "next": {"dgrad": next_rows} if next_rows else None,
+        "next": ({"dgrad": {k: v for k, v in next_rows.items() if not k.startswith("mx_")},
+                  "mxfp4": {k: v for k, v in next_rows.items() if k.startswith("mx_")}}
+                 if next_rows else None),
         "roofline": roofline,
         "cpu_baseline": None,
     }

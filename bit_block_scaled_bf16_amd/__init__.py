@@ -35,6 +35,9 @@ from ._lib import (  # noqa: F401  (re-exported constants and raw entry points)
     nvfp4_rht_quantize,
     nvfp4_rht_sign_mask,
     nvfp4_rht_transform,
+    mxfp4_dequantize,
+    mxfp4_gemm,
+    mxfp4_quantize,
 )
 
 __all__ = [
@@ -151,4 +154,41 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=None, out=None):
     c = out if out is not None else _empty((a.rows, b.rows), out_dtype, a.codes.device)
     nvfp4_gemm(a.codes, a.scales, a.tensor_scale, a.block, b.codes, b.scales, b.tensor_scale,
                b.block, a.rows, b.rows, a.cols, c)
+    return c
+
+
+# ---------------------------------------------------------------------------
+# MXFP4, the comparison format: 32-element blocks along rows, E8M0 scales.
+# ---------------------------------------------------------------------------
+
+
+def mx_quantize(x):
+    """MXFP4 codes [rows, cols/2] and E8M0 scale bytes [rows, cols/32] of x."""
+    import torch
+
+    rows, cols = x.shape
+    q = _empty((rows, cols // 2), torch.uint8, x.device)
+    s = _empty((rows, cols // 32), torch.uint8, x.device)
+    mxfp4_quantize(x, q, s)
+    return q, s
+
+
+def mx_dequantize(q, s, out_dtype=None):
+    import torch
+
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    rows, cols = q.shape[0], q.shape[1] * 2
+    y = _empty((rows, cols), out_dtype, q.device)
+    mxfp4_dequantize(q, s, rows, cols, y)
+    return y
+
+
+def mx_gemm(qa, sa, qb, sb, out_dtype=None, out=None):
+    """C = deq(A) @ deq(B)^T for MXFP4 operands [M, K] and [N, K]."""
+    import torch
+
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    m, n, k = qa.shape[0], qb.shape[0], qa.shape[1] * 2
+    c = out if out is not None else _empty((m, n), out_dtype, qa.device)
+    mxfp4_gemm(qa, sa, qb, sb, m, n, k, c)
     return c

@@ -39,6 +39,9 @@ _SIGNATURES = {
     "nvfp4_rht_transform": (_INT, [_P, _INT, _I64, _I64, _I64, _U64, _P, _P]),
     "nvfp4_rht_sign_mask": (_U32, [_U64]),
     "nvfp4_status_string": (ctypes.c_char_p, [_INT]),
+    "mxfp4_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P]),
+    "mxfp4_dequantize": (_INT, [_P, _P, _I64, _I64, _INT, _P, _I64, _P]),
+    "mxfp4_gemm": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _I64, _P]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -152,6 +155,23 @@ def nvfp4_gemm(qa, sa, ta, a_block, qb, sb, tb, b_block, M, N, K, c, stream=None
     _check("nvfp4_gemm", lib().nvfp4_gemm(
         _ptr(qa), _ptr(sa), _ptr(ta), a_block, _ptr(qb), _ptr(sb), _ptr(tb), b_block, M, N, K,
         _ptr(c), _dtype_code(c), _ld(c), _stream(stream)))
+
+
+def mxfp4_quantize(x, q, s, stream=None) -> None:
+    rows, cols = x.shape
+    _check("mxfp4_quantize", lib().mxfp4_quantize(
+        _ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q), _ptr(s), _stream(stream)))
+
+
+def mxfp4_dequantize(q, s, rows, cols, y, stream=None) -> None:
+    _check("mxfp4_dequantize", lib().mxfp4_dequantize(
+        _ptr(q), _ptr(s), rows, cols, _dtype_code(y), _ptr(y), _ld(y), _stream(stream)))
+
+
+def mxfp4_gemm(qa, sa, qb, sb, M, N, K, c, stream=None) -> None:
+    _check("mxfp4_gemm", lib().mxfp4_gemm(
+        _ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), M, N, K, _ptr(c), _dtype_code(c), _ld(c),
+        _stream(stream)))
 
 
 def nvfp4_philox_fill(seed, c2, c3, n_groups, out, stream=None) -> None:

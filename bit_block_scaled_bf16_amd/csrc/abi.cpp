@@ -226,6 +226,54 @@ int nvfp4_rht_transform(const void* x, int x_dtype, int64_t tokens, int64_t cols
              : NVFP4_ERR_HIP;
 }
 
+int mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                   uint8_t* q, uint8_t* s, hipStream_t stream) {
+  int rc = check_input(x, x_dtype, rows, cols, ldx);
+  if (rc != NVFP4_OK) return rc;
+  if ((cols % 32) != 0) return NVFP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (rows > kMaxElements / cols) return NVFP4_ERR_SHAPE;
+  if (q == nullptr || s == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned16(q) || !aligned16(s)) return NVFP4_ERR_ALIGN;
+  return nvfp4::launch_mx_quantize(x, x_dtype == NVFP4_BF16, rows, cols, ldx, q, s, stream) == 0
+             ? NVFP4_OK
+             : NVFP4_ERR_HIP;
+}
+
+int mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols,
+                     int out_dtype, void* y, int64_t ldy, hipStream_t stream) {
+  if (!valid_dtype(out_dtype)) return NVFP4_ERR_ENUM;
+  if (rows < 0 || cols < 0 || (cols % 32) != 0 || ldy < cols) return NVFP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (rows > kMaxElements / cols) return NVFP4_ERR_SHAPE;
+  if (q == nullptr || s == nullptr || y == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned16(q) || !aligned16(s) || !aligned16(y) || ((ldy * dtype_size(out_dtype)) % 16) != 0)
+    return NVFP4_ERR_ALIGN;
+  return nvfp4::launch_mx_dequantize(q, s, rows, cols, out_dtype == NVFP4_BF16, y, ldy, stream) == 0
+             ? NVFP4_OK
+             : NVFP4_ERR_HIP;
+}
+
+int mxfp4_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
+               int64_t M, int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc,
+               hipStream_t stream) {
+  if (!valid_dtype(c_dtype)) return NVFP4_ERR_ENUM;
+  if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || ldc < N) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (M > kMaxElements / N || (K > 0 && (M > kMaxElements / K || N > kMaxElements / K)))
+    return NVFP4_ERR_SHAPE;
+  if (c == nullptr) return NVFP4_ERR_NULL;
+  if (K > 0 && (qa == nullptr || sa == nullptr || qb == nullptr || sb == nullptr))
+    return NVFP4_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(c) % static_cast<uintptr_t>(dtype_size(c_dtype))) != 0)
+    return NVFP4_ERR_ALIGN;
+  if (K > 0 && (!aligned16(qa) || !aligned16(sa) || !aligned16(qb) || !aligned16(sb)))
+    return NVFP4_ERR_ALIGN;
+  return nvfp4::launch_mx_gemm(qa, sa, qb, sb, M, N, K, c, c_dtype == NVFP4_BF16, ldc, stream) == 0
+             ? NVFP4_OK
+             : NVFP4_ERR_HIP;
+}
+
 }  // extern "C"
 
 namespace nvfp4 {

@@ -44,6 +44,7 @@
 // k of [64h, 64h + 64) and sub-step kk uses k = 64h + 8kk + [0, 8): each lane
 // reads 32 contiguous code bytes of a row with two 16-byte LDS reads.
 #include "device_common.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 #include <atomic>
@@ -51,9 +52,10 @@
 namespace nvfp4 {
 namespace {
 
+using namespace gemm_common;
+
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 128;                 // K elements per step
 constexpr int kThreads = 256;            // 4 waves, 2 x 2 over the tile
@@ -153,9 +155,6 @@ __device__ __forceinline__ Stage<kT> load_stage(const OperandSource<kT>& src, in
   return st;
 }
 
-// Position (in 16-byte units) of code chunk c of LDS row r.
-__device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3); }
-
 // Writes a register-staged step into LDS (swizzled code chunks).
 template <int kT>
 __device__ __forceinline__ void store_stage(uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -204,32 +203,6 @@ __device__ __forceinline__ DmaSource<kT> dma_source(const uint8_t* __restrict__ 
   return d;
 }
 
-// One direct-to-LDS load: every lane fetches kBytes from its own global
-// address and the wave's data lands in lane order at LDS byte address
-// lds_addr (taken from M0, which needs one wait state after it is written).
-// Written as inline assembly so that the compiler does not make unrelated LDS
-// reads wait for it; the kernel itself waits for these loads (vmcnt) before
-// the barrier that hands a stage to the other waves.
-template <int kBytes>
-__device__ __forceinline__ void lds_dma(const uint8_t* gptr, uint32_t lds_addr) {
-  if constexpr (kBytes == 16) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gptr), "s"(lds_addr)
-                 : "memory", "m0");
-  } else {
-    static_assert(kBytes == 4, "4- or 16-byte loads");
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 :
-                 : "v"(gptr), "s"(lds_addr)
-                 : "memory", "m0");
-  }
-}
-
-__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-
 template <int kT>
 __device__ __forceinline__ void dma_stage(const DmaSource<kT>& d, const uint8_t* codes,
                                           const uint8_t* scales, int step, int wave) {
@@ -266,22 +239,6 @@ __device__ __forceinline__ half8_t expand8(uint32_t w, _Float16 sf) {
   const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * s2;
   return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
-
-// Two float32 -> two bf16 (round to nearest even; gfx950 converts a pair in
-// one instruction), low half = a.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
-  const bf16x2_t h = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-// s_waitcnt immediates: wait for every vector memory load (vmcnt 0) and
-// nothing else (expcnt and lgkmcnt fields at their maximum).
-constexpr int kWaitVmcnt0 = 0x0F70;
-
-// Scheduling hints (instruction classes of the gfx9 group scheduler).
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedValu = 0x002;
 
 // The codes of this wave's kT row blocks of A and kT column blocks of B for
 // one step: two uint4 per block, [0] for sub-steps 0-3 and [1] for 4-7.
@@ -514,56 +471,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     cur = nxt;
   }
 
-  // Epilogue: C = acc * (S_A * S_B). The MFMAs took B as their first operand,
-  // so each accumulator tile is C^T in the MFMA output layout: lane l holds
-  // row l % 32 of the 32 x 32 tile and, in elements 4g .. 4g + 3, its four
-  // consecutive columns 8g + 4(l / 32) .. + 3. They leave as one 8-byte (bf16)
-  // or 16-byte (float32) store; ragged edges and unaligned rows fall back to
-  // element stores.
-  const float scale = __fmul_rn(*p.ta, *p.tb);
-  const int row_l = lane & 31;
-  const int col_l = (lane >> 5) * 4;
-  const bool vec_ok = ((p.ldc & 3) == 0) &&
-                      ((reinterpret_cast<uintptr_t>(p.c) & (kBf16Out ? 7u : 15u)) == 0);
-#pragma unroll
-  for (int i = 0; i < kT; ++i) {
-    const int64_t row = m0 + wm * G::kWave + i * 32 + row_l;
-    if (row >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < kT; ++j) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t col = n0 + wn * G::kWave + j * 32 + 8 * g + col_l;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = __fmul_rn(acc[i][j][4 * g + e], scale);
-        if (vec_ok && col + 3 < p.N) {
-          if constexpr (kBf16Out) {
-            const uint32_t lo = f32x2_to_bf16x2(v[0], v[1]);
-            const uint32_t hi = f32x2_to_bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.c) + row * p.ldc + col) = make_uint2(lo, hi);
-          } else {
-            *reinterpret_cast<float4*>(static_cast<float*>(p.c) + row * p.ldc + col) =
-                make_float4(v[0], v[1], v[2], v[3]);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (col + e < p.N) {
-              if constexpr (kBf16Out) {
-                static_cast<uint16_t*>(p.c)[row * p.ldc + col + e] =
-                    static_cast<uint16_t>(f32x2_to_bf16x2(v[e], 0.0f) & 0xFFFFu);
-              } else {
-                static_cast<float*>(p.c)[row * p.ldc + col + e] = v[e];
-              }
-            }
-          }
-        }
-      }
-    }
-  }
+  // Epilogue: C = acc * (S_A * S_B).
+  store_tile<kT, kBf16Out>(acc, __fmul_rn(*p.ta, *p.tb), p.c, p.ldc, p.M, p.N, m0 + wm * G::kWave,
+                           n0 + wn * G::kWave, lane);
 }
 
+}  // namespace
+
+namespace gemm_common {
 __global__ void zero_output_kernel(void* c, int64_t M, int64_t N, int64_t ldc, bool bf16) {
   const int64_t total = M * N;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
@@ -573,6 +488,9 @@ __global__ void zero_output_kernel(void* c, int64_t M, int64_t N, int64_t ldc, b
     else static_cast<float*>(c)[r * ldc + col] = 0.0f;
   }
 }
+}  // namespace gemm_common
+
+namespace {
 
 template <int kT, bool kA2D, bool kB2D>
 int launch_variant(const GemmParams& p, int64_t blocks, bool aligned, bool bf16, hipStream_t stream) {

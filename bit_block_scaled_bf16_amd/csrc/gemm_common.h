@@ -1,0 +1,118 @@
+// Pieces shared by the GEMM kernels on 4-bit operands (NVFP4 and MXFP4):
+// direct-to-LDS loads, the swizzled LDS code layout and the epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+namespace gemm_common {
+
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+// Position (in 16-byte units) of code chunk c of LDS row r. The four 16-byte
+// chunks of a 64-byte code row are XOR-swizzled by (r >> 1 ^ r >> 2) & 3, so
+// both the DMA's contiguous writes and fragment reads of 16 (or 8)
+// consecutive rows hit distinct banks.
+__device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3); }
+
+// One direct-to-LDS load: every lane fetches kBytes from its own global
+// address and the wave's data lands in lane order at LDS byte address
+// lds_addr (taken from M0, which needs one wait state after it is written).
+// Written as inline assembly so that the compiler does not make unrelated LDS
+// reads wait for it; the kernels wait for these loads themselves (vmcnt)
+// before the barrier that hands a stage to the other waves.
+template <int kBytes>
+__device__ __forceinline__ void lds_dma(const uint8_t* gptr, uint32_t lds_addr) {
+  if constexpr (kBytes == 16) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_addr)
+                 : "memory", "m0");
+  } else {
+    static_assert(kBytes == 4, "4- or 16-byte loads");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_addr)
+                 : "memory", "m0");
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// s_waitcnt immediate that waits for every vector memory load (vmcnt 0) and
+// nothing else (expcnt and lgkmcnt fields at their maximum).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Scheduling hints (instruction classes of the gfx9 group scheduler).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedValu = 0x002;
+
+// Two float32 -> two bf16 (round to nearest even; gfx950 converts a pair in
+// one instruction), low half = a.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const bf16x2_t h = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Epilogue of a wave's kT x kT accumulator tiles: C = acc * scale. The MFMAs
+// took B as their first operand, so each accumulator tile is C^T in the MFMA
+// output layout: lane l holds row l % 32 of the 32 x 32 tile and, in elements
+// 4g .. 4g + 3, its four consecutive columns 8g + 4(l / 32) .. + 3. They
+// leave as one 8-byte (bf16) or 16-byte (float32) store; ragged edges and
+// unaligned rows fall back to element stores.
+template <int kT, bool kBf16Out>
+__device__ __forceinline__ void store_tile(const floatx16_t (&acc)[kT][kT], float scale, void* c,
+                                           int64_t ldc, int64_t M, int64_t N, int64_t row0,
+                                           int64_t col0, int lane) {
+  const int row_l = lane & 31;
+  const int col_l = (lane >> 5) * 4;
+  const bool vec_ok = ((ldc & 3) == 0) &&
+                      ((reinterpret_cast<uintptr_t>(c) & (kBf16Out ? 7u : 15u)) == 0);
+#pragma unroll
+  for (int i = 0; i < kT; ++i) {
+    const int64_t row = row0 + i * 32 + row_l;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < kT; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t col = col0 + j * 32 + 8 * g + col_l;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __fmul_rn(acc[i][j][4 * g + e], scale);
+        if (vec_ok && col + 3 < N) {
+          if constexpr (kBf16Out) {
+            const uint32_t lo = f32x2_to_bf16x2(v[0], v[1]);
+            const uint32_t hi = f32x2_to_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(c) + row * ldc + col) = make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(c) + row * ldc + col) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (col + e < N) {
+              if constexpr (kBf16Out) {
+                static_cast<uint16_t*>(c)[row * ldc + col + e] =
+                    static_cast<uint16_t>(f32x2_to_bf16x2(v[e], 0.0f) & 0xFFFFu);
+              } else {
+                static_cast<float*>(c)[row * ldc + col + e] = v[e];
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// Writes zeros to C (the K == 0 product).
+__global__ void zero_output_kernel(void* c, int64_t M, int64_t N, int64_t ldc, bool bf16);
+
+}  // namespace gemm_common
+}  // namespace nvfp4

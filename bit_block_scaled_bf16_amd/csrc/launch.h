@@ -51,6 +51,15 @@ int launch_gemm(const GemmLaunch& g, hipStream_t stream);
 // query fails).
 int device_compute_units();
 
+// MXFP4 (comparison format).
+int launch_mx_quantize(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                       uint8_t* q, uint8_t* s, hipStream_t stream);
+int launch_mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols,
+                         bool out_bf16, void* y, int64_t ldy, hipStream_t stream);
+int launch_mx_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
+                   int64_t M, int64_t N, int64_t K, void* c, bool c_bf16, int64_t ldc,
+                   hipStream_t stream);
+
 int launch_philox_fill(uint64_t seed, uint32_t c2, uint32_t c3, int64_t n_groups, uint32_t* out,
                        hipStream_t stream);
 

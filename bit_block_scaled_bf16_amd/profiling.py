@@ -41,6 +41,7 @@ KERNEL_SOURCES = {
     "quantize_kernel": "quantize.hip",
     "amax_flat_kernel": "quantize.hip",
     "amax_tile_kernel": "quantize.hip",
+    "mxfp4": "mxfp4.hip",
 }
 
 

@@ -218,6 +218,42 @@ uint32_t nvfp4_rht_sign_mask(uint64_t rht_seed);
 /* Host-only: static description of a status code. */
 const char* nvfp4_status_string(int status);
 
+/* ------------------------------------------------------------------------
+ * MXFP4, the comparison format (gist.science summary, Resumen técnico §2
+ * "Formato NVFP4": blocks of 32 elements instead of 16; §1: coarser scale
+ * factors). E2M1 codes packed as NVFP4's; one E8M0 scale byte b per 32
+ * elements along a row, value 2^(b - 127), with b = max(floor(log2 amax) -
+ * 2 + 127, 0) so the block amax maps into [4, 8); elements rounded to nearest
+ * (ties to the even code, saturating at 6); no tensor scale. Non-finite
+ * inputs give unspecified codes.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * mxfp4_quantize -- q [rows][cols/2] codes and s [rows][cols/32] E8M0 scale
+ * bytes of x [rows][ldx] (NVFP4_F32 or NVFP4_BF16). rows, cols >= 0,
+ * cols % 32 == 0, ldx >= cols, every row 16-byte aligned. One pass over x.
+ */
+int mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                   uint8_t* q, uint8_t* s, hipStream_t stream);
+
+/*
+ * mxfp4_dequantize -- y [rows][ldy] = e2m1(q) * 2^(b - 127), as float32 or
+ * bf16 (exact in both). cols % 32 == 0, ldy >= cols.
+ */
+int mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols,
+                     int out_dtype, void* y, int64_t ldy, hipStream_t stream);
+
+/*
+ * mxfp4_gemm -- C[M][N] = sum_k deq(A)[m][k] deq(B)[n][k] with A [M][K] and
+ * B [N][K] in MXFP4 (codes qa/qb, scales sa/sb as mxfp4_quantize writes
+ * them), float32 accumulation on gfx950's block-scaled FP4 MFMA, C in
+ * c_dtype with leading dimension ldc >= N (element alignment suffices).
+ * K % 128 == 0 (K == 0 writes zeros); operand pointers 16-byte aligned.
+ */
+int mxfp4_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
+               int64_t M, int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc,
+               hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,8 @@ def L():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|uint32_t|const char\*)\s+(nvfp4_\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|uint32_t|const char\*)\s+((?:nvfp4|mxfp4)_\w+)\(",
+                                 text, re.M)))
 
 
 def test_header_declares_the_boundary():
@@ -138,6 +139,30 @@ def test_dequantize_and_gemm_argument_errors(L):
     assert g(qa=MIS) == 4
     # empty products enqueue nothing and succeed
     assert g(M=0) == 0 and g(N=0) == 0
+
+
+def test_mxfp4_argument_errors(L):
+    q = lambda **kw: L.mxfp4_quantize(*dict(dict(x=FAKE, xd=1, rows=32, cols=64, ldx=64, q=FAKE,
+                                                 s=FAKE, st=None), **kw).values())
+    assert q(cols=48, ldx=48) == 2   # 32-element blocks
+    assert q(ldx=32) == 2
+    assert q(xd=5) == 3
+    assert q(q=None) == 1
+    assert q(s=MIS) == 4
+    assert q(rows=0) == 0
+    d = lambda **kw: L.mxfp4_dequantize(*dict(dict(q=FAKE, s=FAKE, rows=32, cols=64, od=0, y=FAKE,
+                                                   ldy=64, st=None), **kw).values())
+    assert d(cols=80, ldy=80) == 2
+    assert d(od=7) == 3
+    assert d(y=None) == 1
+    g = lambda **kw: L.mxfp4_gemm(*dict(dict(qa=FAKE, sa=FAKE, qb=FAKE, sb=FAKE, M=32, N=32, K=128,
+                                             c=FAKE, cd=1, ldc=32, st=None), **kw).values())
+    assert g(K=96) == 2              # K steps of 128
+    assert g(ldc=16) == 2
+    assert g(cd=4) == 3
+    assert g(qb=None) == 1
+    assert g(qa=MIS) == 4
+    assert g(N=0) == 0
 
 
 def test_hook_argument_errors(L):
