@@ -45,6 +45,11 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
 * mx.*                -- pinned: E8M0 bytes against float32 exponent fields,
                          the [4, 8) scale invariant, a hand-worked block,
                          power-of-two invariance, a triple loop for the GEMM.
+* fp8.*               -- pinned: torch.float8_e4m3fn cast below 448 (random
+                         values and every midpoint neighbourhood), saturation
+                         and signed zero by hand, tensor-scale closed forms,
+                         exact E4M3 inputs, power-of-two invariance, a
+                         triple loop and an all-ones GEMM.
 """
 
 from .formats import (
@@ -55,6 +60,7 @@ from .formats import (
     e4m3_decode,
     e4m3_encode,
 )
+from .fp8 import FP8_MAX, fp8_dequantize, fp8_encode, fp8_gemm, fp8_quantize, fp8_tensor_scale
 from .mx import MX_BLOCK, e8m0_decode, mx_dequantize, mx_gemm, mx_quantize, mx_scale_bytes
 from .philox import philox4x32_10, sr_random_u16
 from .hadamard import hadamard16, rht_signs, rht
@@ -72,6 +78,12 @@ from .quantize import (
 from .gemm import gemm
 
 __all__ = [
+    "FP8_MAX",
+    "fp8_dequantize",
+    "fp8_encode",
+    "fp8_gemm",
+    "fp8_quantize",
+    "fp8_tensor_scale",
     "MX_BLOCK",
     "e8m0_decode",
     "mx_dequantize",
