@@ -35,6 +35,7 @@ METRIC = "NVFP4 quantize GB/s (% HBM peak) + NVFP4 GEMM TFLOP/s (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 MFMA, MI355X
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # dense FP4 MFMA (the MXFP4 comparison GEMM), MI355X
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense FP8 MFMA (the FP8 baseline GEMMs), MI355X
 
 TOKENS, HIDDEN, FFN = 16384, 5120, 20480
 
@@ -62,10 +63,29 @@ CALL_KERNELS = {
     "gemm_dgrad": (("gemm_kernel<4, false, true,", 1), ("gemm_kernel<2, false, true,", 1)),
     "mx_quantize_x": (("mx_quantize_kernel<unsigned short>", 0),),
     "mx_quantize_w": (("mx_quantize_kernel<unsigned short>", 1),),
-    "mx_gemm_fprop": (("mx_gemm_kernel<true>", 0),),
+    "mx_gemm_fprop": (("block_gemm_kernel<(Fmt)0", 0),),
+    "fp8_quantize_x": (("amax_flat_kernel<unsigned short>", 3),
+                       ("fp8_quantize_kernel<unsigned short>", 0)),
+    "fp8_quantize_w": (("amax_flat_kernel<unsigned short>", 4),
+                       ("fp8_quantize_kernel<unsigned short>", 1)),
+    "fp8_quantize_dy": (("amax_flat_kernel<unsigned short>", 5),
+                        ("fp8_quantize_kernel<unsigned short>", 2)),
+    "fp8_gemm_fprop": (("block_gemm_kernel<(Fmt)1", 0),),
+    "fp8_gemm_wgrad": (("block_gemm_kernel<(Fmt)1", 1),),
 }
-CALL_SOURCE = {n: ("mxfp4" if n.startswith("mx_") else
-                   "gemm_kernel" if n.startswith("gemm") else "quantize_kernel") for n in CALL_KERNELS}
+
+
+def _call_source(name):
+    if name.startswith("mx_gemm") or name.startswith("fp8_gemm"):
+        return "f8f6f4_gemm"
+    if name.startswith("mx_"):
+        return "mxfp4"
+    if name.startswith("fp8_"):
+        return ("fp8", "quantize_kernel")  # its amax pass is the NVFP4 quantizer's
+    return "gemm_kernel" if name.startswith("gemm") else "quantize_kernel"
+
+
+CALL_SOURCE = {n: _call_source(n) for n in CALL_KERNELS}
 
 
 def parse():
@@ -113,6 +133,11 @@ class Step:
         # MXFP4 comparison: X and W in 1x32 blocks, fprop on the FP4 MFMA
         self.mqx, self.msx = e(t, h // 2), e(t, h // 32)
         self.mqw, self.msw = e(f, h // 2), e(f, h // 32)
+        # FP8 baseline (E4M3, per tensor): X row + column copies, W row copy,
+        # dY column copy; fprop Y = X W^T and wgrad dW = dY^T X
+        self.fx, self.fxt, self.ftx, self.fax = e(t, h), e(h, t), sc(), ws()
+        self.fw, self.ftw, self.faw = e(f, h), sc(), ws()
+        self.fdyt, self.ftdy, self.fady = e(f, t), sc(), ws()
         self.y = torch.empty((t, f), dtype=torch.bfloat16, device=dev)
         self.dw = torch.empty((f, h), dtype=torch.bfloat16, device=dev)
         self.status = torch.zeros(4, dtype=torch.int32, device=dev)
@@ -165,6 +190,22 @@ class Step:
                                                     s.y)),
         ]
 
+    def fp8_calls(self):
+        """The FP8 baseline (fprop and wgrad), timed apart from the step."""
+        nv = self.nv
+        s = self
+        return [
+            ("fp8_quantize_x", lambda: nv.fp8_quantize(s.x, nv.OUT_ROW | nv.OUT_COL, None, s.fax,
+                                                       s.fx, s.fxt, s.ftx, s.status)),
+            ("fp8_quantize_w", lambda: nv.fp8_quantize(s.w, nv.OUT_ROW, None, s.faw, s.fw, None,
+                                                       s.ftw, s.status)),
+            ("fp8_quantize_dy", lambda: nv.fp8_quantize(s.dy, nv.OUT_COL, None, s.fady, None,
+                                                        s.fdyt, s.ftdy, s.status)),
+            ("fp8_gemm_fprop", lambda: nv.fp8_gemm(s.fx, s.ftx, s.fw, s.ftw, s.t, s.f, s.h, s.y)),
+            ("fp8_gemm_wgrad", lambda: nv.fp8_gemm(s.fdyt, s.ftdy, s.fxt, s.ftx, s.f, s.h, s.t,
+                                                   s.dw)),
+        ]
+
     def work(self):
         """Algorithmic bytes (quantizer calls, amax pass included) or flops."""
         t, h, f = self.t, self.h, self.f
@@ -182,6 +223,12 @@ class Step:
             "mx_quantize_x": ("GB/s", t * h * (2 + 0.5 + 1.0 / 32)),
             "mx_quantize_w": ("GB/s", f * h * (2 + 0.5 + 1.0 / 32)),
             "mx_gemm_fprop": ("FP4 TFLOP/s", 2.0 * t * f * h),
+            # FP8: amax pass + quantize pass over bf16, one byte out per copy
+            "fp8_quantize_x": ("GB/s", t * h * (2 + 2 + 2)),
+            "fp8_quantize_w": ("GB/s", f * h * (2 + 2 + 1)),
+            "fp8_quantize_dy": ("GB/s", t * f * (2 + 2 + 1)),
+            "fp8_gemm_fprop": ("FP8 TFLOP/s", 2.0 * t * f * h),
+            "fp8_gemm_wgrad": ("FP8 TFLOP/s", 2.0 * f * h * t),
         }
 
 
@@ -277,7 +324,7 @@ def main():
     assert int(step.status.cpu()[0]) == 0, "non-finite amax"
 
     # the dgrad path, after the timed step and outside it
-    next_calls = [] if args.no_next else step.next_calls() + step.mx_calls()
+    next_calls = [] if args.no_next else step.next_calls() + step.mx_calls() + step.fp8_calls()
     for _ in range(min(args.warmup, 1)):
         for _, fn in next_calls:
             fn()
@@ -308,7 +355,8 @@ def main():
                 peak = HBM_PEAK_GBS
             else:
                 rate = amount / (avg_ms * 1e-3) / 1e12
-                peak = FP4_MFMA_PEAK_TFLOPS if unit.startswith("FP4") else MFMA_PEAK_TFLOPS
+                peak = (FP4_MFMA_PEAK_TFLOPS if unit.startswith("FP4") else
+                        FP8_MFMA_PEAK_TFLOPS if unit.startswith("FP8") else MFMA_PEAK_TFLOPS)
             res[name] = {"us": round(avg_ms * 1e3, 2), "achieved": round(rate, 1), "unit": unit,
                          "frac": round(rate / peak, 4), "work": amount,
                          "traffic": profiling.kernel_traffic(summary, CALL_KERNELS[name],
@@ -361,8 +409,10 @@ def main():
                  "frac": round(gemm_flops / (g_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4),
                  "us": round(g_us, 1)},
         "kernels": kernels,
-        "next": ({"dgrad": {k: v for k, v in next_rows.items() if not k.startswith("mx_")},
-                  "mxfp4": {k: v for k, v in next_rows.items() if k.startswith("mx_")}}
+        "next": ({"dgrad": {k: v for k, v in next_rows.items()
+                            if not k.startswith("mx_") and not k.startswith("fp8_")},
+                  "mxfp4": {k: v for k, v in next_rows.items() if k.startswith("mx_")},
+                  "fp8": {k: v for k, v in next_rows.items() if k.startswith("fp8_")}}
                  if next_rows else None),
         "roofline": roofline,
         "cpu_baseline": None,

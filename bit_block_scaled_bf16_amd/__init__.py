@@ -38,6 +38,9 @@ from ._lib import (  # noqa: F401  (re-exported constants and raw entry points)
     mxfp4_dequantize,
     mxfp4_gemm,
     mxfp4_quantize,
+    fp8_dequantize,
+    fp8_gemm,
+    fp8_quantize,
 )
 
 __all__ = [
@@ -191,4 +194,44 @@ def mx_gemm(qa, sa, qb, sb, out_dtype=None, out=None):
     m, n, k = qa.shape[0], qb.shape[0], qa.shape[1] * 2
     c = out if out is not None else _empty((m, n), out_dtype, qa.device)
     mxfp4_gemm(qa, sa, qb, sb, m, n, k, c)
+    return c
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3, one scale per tensor), the baseline format.
+# ---------------------------------------------------------------------------
+
+
+def f8_quantize(x, outputs: int = OUT_ROW, amax_ws=None):
+    """FP8 copies of x: (row bytes [rows, cols] or None, column bytes
+    [cols, rows] or None, decode scale S8 as a float32 [4] tensor)."""
+    import torch
+
+    rows, cols = x.shape
+    q_row = _empty((rows, cols), torch.uint8, x.device) if outputs & OUT_ROW else None
+    q_col = _empty((cols, rows), torch.uint8, x.device) if outputs & OUT_COL else None
+    ts = _scalar(x.device)
+    ws = amax_ws if amax_ws is not None else amax_workspace(x.device)
+    fp8_quantize(x, outputs, None, ws, q_row, q_col, ts)
+    return q_row, q_col, ts
+
+
+def f8_dequantize(q, tensor_scale, out_dtype=None):
+    import torch
+
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    rows, cols = q.shape
+    y = _empty((rows, cols), out_dtype, q.device)
+    fp8_dequantize(q, tensor_scale, rows, cols, y)
+    return y
+
+
+def f8_gemm(qa, ta, qb, tb, out_dtype=None, out=None):
+    """C = S8_a S8_b e4m3(A) @ e4m3(B)^T for FP8 operands [M, K] and [N, K]."""
+    import torch
+
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    m, n, k = qa.shape[0], qb.shape[0], qa.shape[1]
+    c = out if out is not None else _empty((m, n), out_dtype, qa.device)
+    fp8_gemm(qa, ta, qb, tb, m, n, k, c)
     return c

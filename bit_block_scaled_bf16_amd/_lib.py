@@ -42,6 +42,9 @@ _SIGNATURES = {
     "mxfp4_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P]),
     "mxfp4_dequantize": (_INT, [_P, _P, _I64, _I64, _INT, _P, _I64, _P]),
     "mxfp4_gemm": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _I64, _P]),
+    "fp8_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P, _P, _P]),
+    "fp8_dequantize": (_INT, [_P, _P, _I64, _I64, _INT, _P, _I64, _P]),
+    "fp8_gemm": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _I64, _P]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -171,6 +174,25 @@ def mxfp4_dequantize(q, s, rows, cols, y, stream=None) -> None:
 def mxfp4_gemm(qa, sa, qb, sb, M, N, K, c, stream=None) -> None:
     _check("mxfp4_gemm", lib().mxfp4_gemm(
         _ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), M, N, K, _ptr(c), _dtype_code(c), _ld(c),
+        _stream(stream)))
+
+
+def fp8_quantize(x, outputs, amax_in, amax_ws, q_row, q_col, tensor_scale, dev_status=None,
+                 stream=None) -> None:
+    rows, cols = x.shape
+    _check("fp8_quantize", lib().fp8_quantize(
+        _ptr(x), _dtype_code(x), rows, cols, _ld(x), outputs, _ptr(amax_in), _ws(amax_ws),
+        _ptr(q_row), _ptr(q_col), _ptr(tensor_scale), _ptr(dev_status), _stream(stream)))
+
+
+def fp8_dequantize(q, tensor_scale, rows, cols, y, stream=None) -> None:
+    _check("fp8_dequantize", lib().fp8_dequantize(
+        _ptr(q), _ptr(tensor_scale), rows, cols, _dtype_code(y), _ptr(y), _ld(y), _stream(stream)))
+
+
+def fp8_gemm(qa, ta, qb, tb, M, N, K, c, stream=None) -> None:
+    _check("fp8_gemm", lib().fp8_gemm(
+        _ptr(qa), _ptr(ta), _ptr(qb), _ptr(tb), M, N, K, _ptr(c), _dtype_code(c), _ld(c),
         _stream(stream)))
 
 

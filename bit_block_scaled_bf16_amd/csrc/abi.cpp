@@ -274,6 +274,73 @@ int mxfp4_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const ui
              : NVFP4_ERR_HIP;
 }
 
+int fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int outputs,
+                 const float* amax_in, float* amax_ws, uint8_t* q_row, uint8_t* q_col,
+                 float* tensor_scale, int32_t* dev_status, hipStream_t stream) {
+  if (outputs < 1 || outputs > 3) return NVFP4_ERR_ENUM;
+  int rc = check_input(x, x_dtype, rows, cols, ldx);
+  if (rc != NVFP4_OK) return rc;
+  const bool out_row = (outputs & NVFP4_OUT_ROW) != 0, out_col = (outputs & NVFP4_OUT_COL) != 0;
+  if (out_col && (rows % 16) != 0) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && cols > kMaxElements / rows) return NVFP4_ERR_SHAPE;
+  if (tensor_scale == nullptr) return NVFP4_ERR_NULL;
+  if (amax_in == nullptr && amax_ws == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned16(tensor_scale) || (amax_in && !aligned16(amax_in)) ||
+      (amax_ws && !aligned16(amax_ws)) || (dev_status && !aligned16(dev_status)))
+    return NVFP4_ERR_ALIGN;
+  if (rows > 0 && cols > 0) {
+    if ((out_row && q_row == nullptr) || (out_col && q_col == nullptr)) return NVFP4_ERR_NULL;
+    if ((out_row && !aligned16(q_row)) || (out_col && !aligned16(q_col))) return NVFP4_ERR_ALIGN;
+  }
+  nvfp4::Fp8QuantizeLaunch q;
+  q.x = x;
+  q.x_bf16 = x_dtype == NVFP4_BF16;
+  q.rows = rows;
+  q.cols = cols;
+  q.ldx = ldx;
+  q.outputs = outputs;
+  q.amax_in = amax_in;
+  q.amax_ws = amax_ws;
+  q.q_row = q_row;
+  q.q_col = q_col;
+  q.tensor_scale = tensor_scale;
+  q.dev_status = dev_status;
+  return nvfp4::launch_fp8_quantize(q, stream) == 0 ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+int fp8_dequantize(const uint8_t* q, const float* tensor_scale, int64_t rows, int64_t cols,
+                   int out_dtype, void* y, int64_t ldy, hipStream_t stream) {
+  if (!valid_dtype(out_dtype)) return NVFP4_ERR_ENUM;
+  if (rows < 0 || cols < 0 || (cols % 16) != 0 || ldy < cols) return NVFP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (rows > kMaxElements / cols) return NVFP4_ERR_SHAPE;
+  if (q == nullptr || tensor_scale == nullptr || y == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned16(q) || !aligned16(y) || ((ldy * dtype_size(out_dtype)) % 16) != 0)
+    return NVFP4_ERR_ALIGN;
+  return nvfp4::launch_fp8_dequantize(q, tensor_scale, rows, cols, out_dtype == NVFP4_BF16, y, ldy,
+                                      stream) == 0
+             ? NVFP4_OK
+             : NVFP4_ERR_HIP;
+}
+
+int fp8_gemm(const uint8_t* qa, const float* ta, const uint8_t* qb, const float* tb, int64_t M,
+             int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc, hipStream_t stream) {
+  if (!valid_dtype(c_dtype)) return NVFP4_ERR_ENUM;
+  if (M < 0 || N < 0 || K < 0 || (K % 64) != 0 || ldc < N) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (M > kMaxElements / N || (K > 0 && (M > kMaxElements / K || N > kMaxElements / K)))
+    return NVFP4_ERR_SHAPE;
+  if (c == nullptr) return NVFP4_ERR_NULL;
+  if (K > 0 && (qa == nullptr || qb == nullptr || ta == nullptr || tb == nullptr))
+    return NVFP4_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(c) % static_cast<uintptr_t>(dtype_size(c_dtype))) != 0)
+    return NVFP4_ERR_ALIGN;
+  if (K > 0 && (!aligned16(qa) || !aligned16(qb))) return NVFP4_ERR_ALIGN;
+  return nvfp4::launch_fp8_gemm(qa, ta, qb, tb, M, N, K, c, c_dtype == NVFP4_BF16, ldc, stream) == 0
+             ? NVFP4_OK
+             : NVFP4_ERR_HIP;
+}
+
 }  // extern "C"
 
 namespace nvfp4 {

@@ -241,4 +241,38 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// Tensor amax workspace (floats): [0] receives the amax, the per-workgroup
+// partial maxima of the amax kernels (float bits, which order like unsigned
+// integers for non-negative values, NaN above infinity) start at
+// kPartialsOffset.
+// ---------------------------------------------------------------------------
+constexpr int kPartialsOffset = 64;
+constexpr int kMaxPartials = 1024;
+
+// The tensor amax from n <= kMaxPartials partial maxima. Each wave reduces
+// them on its own: 4 loads of 16 bytes per lane, all issued before the
+// first is needed (entries past n hold stale values and are masked off,
+// and the loads stay inside the workspace), then a wave maximum: no LDS, no
+// barrier.
+__device__ __forceinline__ float reduce_partials(const uint32_t* __restrict__ partials, int n) {
+  const int lane = threadIdx.x & 63;
+  const uint4* p4 = reinterpret_cast<const uint4*>(partials);
+  uint4 b[kMaxPartials / 256];
+#pragma unroll
+  for (int k = 0; k < kMaxPartials / 256; ++k) b[k] = p4[lane + 64 * k];
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxPartials / 256; ++k) {
+    const int i = 4 * (lane + 64 * k);
+    const uint32_t v[4] = {b[k].x, b[k].y, b[k].z, b[k].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t x = i + c < n ? v[c] : 0u;
+      m = x > m ? x : m;
+    }
+  }
+  return __uint_as_float(wave_max_u32(m));
+}
+
 }  // namespace nvfp4

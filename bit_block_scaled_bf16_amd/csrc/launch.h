@@ -60,6 +60,31 @@ int launch_mx_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, cons
                    int64_t M, int64_t N, int64_t K, void* c, bool c_bf16, int64_t ldc,
                    hipStream_t stream);
 
+// Per-workgroup partial maxima of |x| (no transform) into amax_ws from
+// kPartialsOffset on; returns their count (> 0), or -1 on a launch error.
+// rows and cols are > 0.
+int launch_tensor_amax(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                       float* amax_ws, hipStream_t stream);
+
+// FP8 (E4M3, one scale per tensor; the baseline format).
+struct Fp8QuantizeLaunch {
+  const void* x;
+  bool x_bf16;
+  int64_t rows, cols, ldx;
+  int outputs;  // bit 0: row copy [rows][cols], bit 1: column copy [cols][rows]
+  const float* amax_in;
+  float* amax_ws;
+  uint8_t *q_row, *q_col;
+  float* tensor_scale;
+  int32_t* dev_status;
+};
+int launch_fp8_quantize(const Fp8QuantizeLaunch& q, hipStream_t stream);
+int launch_fp8_dequantize(const uint8_t* q, const float* tensor_scale, int64_t rows, int64_t cols,
+                          bool out_bf16, void* y, int64_t ldy, hipStream_t stream);
+int launch_fp8_gemm(const uint8_t* qa, const float* ta, const uint8_t* qb, const float* tb,
+                    int64_t M, int64_t N, int64_t K, void* c, bool c_bf16, int64_t ldc,
+                    hipStream_t stream);
+
 int launch_philox_fill(uint64_t seed, uint32_t c2, uint32_t c3, int64_t n_groups, uint32_t* out,
                        hipStream_t stream);
 

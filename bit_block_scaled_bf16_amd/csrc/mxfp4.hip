@@ -1,5 +1,6 @@
-// MXFP4, the comparison format of the pages, for gfx950: a 1x32 quantizer,
-// its dequantizer, and a GEMM on the chip's block-scaled FP4 MFMA.
+// MXFP4, the comparison format of the pages, for gfx950: a 1x32 quantizer
+// and its dequantizer (the GEMM on the block-scaled FP4 MFMA is in
+// f8f6f4_gemm.hip).
 //
 // Source: gist.science summary of "Pretraining Large Language Models with
 // NVFP4", Resumen técnico §2 "Formato NVFP4" (MXFP4 uses blocks of 32
@@ -7,22 +8,6 @@
 // E2M1 codes, one E8M0 scale 2^(b - 127) per 32 elements along a row, b
 // chosen so the block amax maps into [4, 8), round to nearest even, no
 // tensor scale. Codes are packed as NVFP4's (even element in the low nibble).
-//
-// GEMM. v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands multiplies a
-// 32 x 64 slice of A by a 32 x 64 slice of B with one E8M0 scale per row
-// and 32 K: lane l supplies row l % 32 and the 32 K values of half l / 32
-// (16 bytes) plus that block's scale byte. This is MXFP4's own definition,
-// so the codes and scale bytes go to the MFMA as stored: no expansion, and
-// the relevant peak is dense FP4 (10.1 PFLOP/s). The staging (256 x 256
-// tile, 4 waves of 128 x 128, K steps of 128 into an LDS ring filled by
-// global_load_lds, XOR-swizzled 64-byte code rows) is the NVFP4 GEMM's; a
-// step is 2 MFMA sub-steps of K = 64 instead of 8 of K = 16, a quarter of
-// the time, so the ring has 4 stages and a step's loads are requested 4
-// steps ahead (the wait before a step's barrier leaves the 2 newest steps'
-// loads in flight). Lane
-// half h takes K [64h, 64h + 64) of a step, sub-step s its 32 values from
-// 64h + 32s, so its two scale bytes of the step are adjacent and one 16-bit
-// LDS read serves both sub-steps (the MFMA's op_sel picks the byte).
 #include "device_common.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -30,7 +15,7 @@
 namespace nvfp4 {
 namespace {
 
-using namespace gemm_common;
+using gemm_common::f32x2_to_bf16x2;
 
 constexpr int kMxBlock = 32;
 
@@ -154,188 +139,6 @@ __global__ __launch_bounds__(256) void mx_dequantize_kernel(const uint8_t* __res
   }
 }
 
-// ---------------------------------------------------------------------------
-// GEMM.
-// ---------------------------------------------------------------------------
-constexpr int kBK = 128;                  // K elements per step
-constexpr int kThreads = 256;
-constexpr int kStages = 4;                // DMA runs 4 steps ahead (a step is short)
-constexpr int kTile = 256;                // C rows and columns per workgroup
-constexpr int kWave = 128;                // C rows and columns per wave
-constexpr int kCodeStride = kBK / 2;      // 64 bytes per LDS code row
-constexpr int kScaleStride = kBK / 32;    // 4 scale bytes per LDS row
-constexpr int kCodeBytes = kTile * kCodeStride;
-constexpr int kScaleBytes = kTile * kScaleStride;
-constexpr int kStageBytes = 2 * kCodeBytes + 2 * kScaleBytes;
-
-typedef int int8v_t __attribute__((ext_vector_type(8)));
-
-struct MxGemmParams {
-  const uint8_t *qa, *sa, *qb, *sb;
-  void* c;
-  int64_t M, N, K, ldc;
-};
-
-// This lane's share of one operand's DMA per step: 4 code chunks (rows
-// 64 w + 16 i + l / 4, LDS position l % 4) and the 4 scale bytes of row
-// 64 w + l. Rows past the end are clamped (they only feed C outside M x N).
-struct MxDmaSource {
-  const uint8_t* q[4];
-  const uint8_t* s;
-};
-
-__device__ __forceinline__ MxDmaSource mx_dma_source(const uint8_t* __restrict__ q,
-                                                     const uint8_t* __restrict__ s, int64_t row0,
-                                                     int64_t rows, int64_t K, int wave, int lane) {
-  MxDmaSource d;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 64 * wave + 16 * i + (lane >> 2);
-    const int64_t row = row0 + r;
-    const int64_t rc = row < rows ? row : rows - 1;
-    d.q[i] = q + rc * (K >> 1) + 16 * chunk_pos(r, lane & 3);
-  }
-  const int64_t row = row0 + 64 * wave + lane;
-  const int64_t rc = row < rows ? row : rows - 1;
-  d.s = s + rc * (K / kMxBlock);
-  return d;
-}
-
-__device__ __forceinline__ void mx_dma_stage(const MxDmaSource& d, const uint8_t* codes,
-                                             const uint8_t* scales, int step, int wave) {
-  const int64_t k0 = static_cast<int64_t>(step) * kBK;
-  const uint32_t c0 = lds_address(codes) + 64 * wave * kCodeStride;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lds_dma<16>(d.q[i] + (k0 >> 1), c0 + 16 * i * kCodeStride);
-  lds_dma<4>(d.s + k0 / kMxBlock, lds_address(scales) + 64 * wave * kScaleStride);
-}
-
-// The fragments of one step: codes [row or column block][sub-step] and the
-// two scale bytes of each block (byte s for sub-step s).
-struct MxFrags {
-  uint4 a[4][2], b[4][2];
-  uint32_t sa[4], sb[4];
-};
-
-struct MxOffsets {
-  int a_code[2], b_code[2], a_scale, b_scale;
-};
-
-__device__ __forceinline__ void mx_read_frags(MxFrags& f, const uint8_t* __restrict__ stage,
-                                              const MxOffsets& o) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      f.a[i][s] = *reinterpret_cast<const uint4*>(stage + o.a_code[s] + i * 32 * kCodeStride);
-      f.b[i][s] = *reinterpret_cast<const uint4*>(stage + kCodeBytes + o.b_code[s] + i * 32 * kCodeStride);
-    }
-    f.sa[i] = *reinterpret_cast<const uint16_t*>(stage + 2 * kCodeBytes + o.a_scale + i * 32 * kScaleStride);
-    f.sb[i] = *reinterpret_cast<const uint16_t*>(stage + 2 * kCodeBytes + kScaleBytes + o.b_scale +
-                                                 i * 32 * kScaleStride);
-  }
-}
-
-__device__ __forceinline__ int8v_t as_operand(const uint4& v) {
-  return int8v_t{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z),
-                 static_cast<int>(v.w), 0, 0, 0, 0};
-}
-
-template <int kS>
-__device__ __forceinline__ void mx_substep(floatx16_t (&acc)[4][4], const MxFrags& f) {
-  // FP4 (E2M1) operands: format code 4 for both; op_sel kS picks the scale
-  // byte of sub-step kS. B goes first, so each accumulator tile is C^T.
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          as_operand(f.b[j][kS]), as_operand(f.a[i][kS]), acc[i][j], 4, 4, kS,
-          static_cast<int>(f.sb[j]), kS, static_cast<int>(f.sa[i]));
-}
-
-// s_waitcnt immediate: at most n vector memory loads outstanding (vmcnt is
-// 6 bits, split over bits 3:0 and 15:14), expcnt and lgkmcnt not waited for.
-constexpr int wait_vmcnt(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
-constexpr int kDmaPerStep = 2 * (4 + 1);  // per wave: 4 code and 1 scale loads per operand
-
-template <bool kBf16Out>
-__global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(MxGemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStageBytes];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t tiles_n = (p.N + kTile - 1) / kTile;
-  const int64_t t = blockIdx.x;
-  const int64_t m0 = (t / tiles_n) * kTile, n0 = (t - (t / tiles_n) * tiles_n) * kTile;
-  const int64_t K = p.K;
-  const int nsteps = static_cast<int>(K / kBK);  // >= 1 (K % 128 == 0, K > 0)
-  const int last = nsteps - 1;
-
-  floatx16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const MxDmaSource da = mx_dma_source(p.qa, p.sa, m0, p.M, K, wave_u, lane);
-  const MxDmaSource db = mx_dma_source(p.qb, p.sb, n0, p.N, K, wave_u, lane);
-  // prologue: steps 0-3 into stages 0-3; steps 0 and 1 must have landed
-#pragma unroll
-  for (int q = 0; q < kStages; ++q) {
-    uint8_t* st = lds + q * kStageBytes;
-    const int ld = q < last ? q : last;
-    mx_dma_stage(da, st, st + 2 * kCodeBytes, ld, wave_u);
-    mx_dma_stage(db, st + kCodeBytes, st + 2 * kCodeBytes + kScaleBytes, ld, wave_u);
-  }
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kDmaPerStep));
-  __syncthreads();
-
-  const int frag_row = lane & 31;
-  const int half = lane >> 5;
-  const int swz = ((frag_row >> 1) ^ (frag_row >> 2)) & 3;  // same for frag_row + 32 i
-  MxOffsets o;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    o.a_code[s] = (wm * kWave + frag_row) * kCodeStride + 16 * ((2 * half + s) ^ swz);
-    o.b_code[s] = (wn * kWave + frag_row) * kCodeStride + 16 * ((2 * half + s) ^ swz);
-  }
-  o.a_scale = (wm * kWave + frag_row) * kScaleStride + 2 * half;
-  o.b_scale = (wn * kWave + frag_row) * kScaleStride + 2 * half;
-
-  // Step s reads step s + 1's fragments from LDS (landed before the barrier
-  // that ended step s - 1) while its own MFMAs run, and requests step s + 4
-  // into stage s % 4: step s's own fragments were read during step s - 1,
-  // before that barrier (for step 0: before the second prologue barrier).
-  // Before a step's barrier, step s + 2 must have landed; the loads of steps
-  // s + 3 and s + 4 stay in flight (loads complete in issue order).
-  MxFrags cur, nxt;
-  mx_read_frags(cur, lds, o);
-  __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
-    const int stage = step & (kStages - 1);
-    const int sn = (step + 1) & (kStages - 1);
-    // the LDS reads go first: the DMA's inline assembly is a compiler
-    // memory barrier, and reads placed after it would sink below the MFMAs
-    mx_read_frags(nxt, lds + sn * kStageBytes, o);
-    {
-      uint8_t* st = lds + stage * kStageBytes;
-      const int ld = (step + kStages) < last ? (step + kStages) : last;
-      mx_dma_stage(da, st, st + 2 * kCodeBytes, ld, wave_u);
-      mx_dma_stage(db, st + kCodeBytes, st + 2 * kCodeBytes + kScaleBytes, ld, wave_u);
-    }
-    mx_substep<0>(acc, cur);
-    mx_substep<1>(acc, cur);
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kDmaPerStep));
-    __syncthreads();
-    cur = nxt;
-  }
-  store_tile<4, kBf16Out>(acc, 1.0f, p.c, p.ldc, p.M, p.N, m0 + wm * kWave, n0 + wn * kWave, lane);
-}
-
 }  // namespace
 
 int launch_mx_quantize(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ldx,
@@ -359,22 +162,6 @@ int launch_mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64
   const int64_t gy = (rows + 7) / 8;
   const dim3 grid(static_cast<unsigned>((nblk + 31) / 32), static_cast<unsigned>(gy < 65535 ? gy : 65535));
   mx_dequantize_kernel<<<grid, 256, 0, stream>>>(q, s, rows, cols, out_bf16, y, ldy);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-int launch_mx_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
-                   int64_t M, int64_t N, int64_t K, void* c, bool c_bf16, int64_t ldc,
-                   hipStream_t stream) {
-  if (K == 0) {
-    int64_t blocks = (M * N + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    zero_output_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(c, M, N, ldc, c_bf16);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
-  }
-  MxGemmParams p{qa, sa, qb, sb, c, M, N, K, ldc};
-  const int64_t tiles = ((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile);
-  if (c_bf16) mx_gemm_kernel<true><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(p);
-  else mx_gemm_kernel<false><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

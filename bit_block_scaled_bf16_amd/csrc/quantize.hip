@@ -144,13 +144,8 @@ __device__ __forceinline__ void rht_columns(float (&v)[16][8], uint32_t sign_mas
   }
 }
 
-// Workspace of the tensor amax (floats): [0] receives the amax, the
-// per-workgroup partial maxima (float bits, which order like unsigned
-// integers for non-negative values, NaN above infinity) start at
-// kPartialsOffset. Partials instead of one atomic maximum need no zeroed
-// word before the reduction, so a call is two kernels, not three.
-constexpr int kPartialsOffset = 64;
-constexpr int kMaxPartials = 1024;
+// Partials instead of one atomic maximum need no zeroed word before the
+// reduction, so a call is two kernels, not three.
 static_assert(kPartialsOffset + kMaxPartials <= NVFP4_AMAX_WS_BYTES / 4, "workspace size");
 static_assert(kMaxTileBlocks <= kMaxPartials, "one partial per workgroup");
 
@@ -321,31 +316,6 @@ __global__ __launch_bounds__(kThreads) void amax_tile_kernel(const InT* __restri
     }
   }
   block_max_store(m, lds4, partials + blockIdx.x);
-}
-
-// The tensor amax from n <= kMaxPartials partial maxima. Each wave reduces
-// them on its own: 4 loads of 16 bytes per lane, all issued before the
-// first is needed (entries past n hold stale values and are masked off,
-// and the loads stay inside the workspace), then a wave maximum: no LDS, no
-// barrier.
-__device__ __forceinline__ float reduce_partials(const uint32_t* __restrict__ partials, int n) {
-  const int lane = threadIdx.x & 63;
-  const uint4* p4 = reinterpret_cast<const uint4*>(partials);
-  uint4 b[kMaxPartials / 256];
-#pragma unroll
-  for (int k = 0; k < kMaxPartials / 256; ++k) b[k] = p4[lane + 64 * k];
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < kMaxPartials / 256; ++k) {
-    const int i = 4 * (lane + 64 * k);
-    const uint32_t v[4] = {b[k].x, b[k].y, b[k].z, b[k].w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t x = i + c < n ? v[c] : 0u;
-      m = x > m ? x : m;
-    }
-  }
-  return __uint_as_float(wave_max_u32(m));
 }
 
 // Writes the tensor scale (and the status) for an empty tensor.
@@ -805,6 +775,12 @@ int launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
 }  // namespace nvfp4
 
 namespace nvfp4 {
+
+int launch_tensor_amax(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                       float* amax_ws, hipStream_t stream) {
+  return x_bf16 ? launch_amax(static_cast<const uint16_t*>(x), rows, cols, ldx, false, 0u, amax_ws, stream)
+                : launch_amax(static_cast<const float*>(x), rows, cols, ldx, false, 0u, amax_ws, stream);
+}
 
 int launch_rht_transform(const void* x, bool x_bf16, int64_t tokens, int64_t cols, int64_t ldx,
                          uint32_t sign_mask, float* out, hipStream_t stream) {

@@ -42,6 +42,10 @@ KERNEL_SOURCES = {
     "amax_flat_kernel": "quantize.hip",
     "amax_tile_kernel": "quantize.hip",
     "mxfp4": "mxfp4.hip",
+    "fp8": "fp8.hip",
+    "f8f6f4_gemm": "f8f6f4_gemm.hip",
+    "fp8_quantize_kernel": "fp8.hip",
+    "block_gemm_kernel": "f8f6f4_gemm.hip",
 }
 
 
@@ -164,18 +168,19 @@ def load_traffic(md_path: str):
     return json.loads(m.group(1)) if m else None
 
 
-def kernel_traffic(md_path: str, kernels, source_key: str):
+def kernel_traffic(md_path: str, kernels, source_key):
     """HBM bytes (read + write) of one call: the sum over `kernels`, a list of
     (short-name fragment, dispatch index) pairs, of that dispatch of the
     first kernel whose short name contains the fragment. None when the
     summary is missing, none of the kernels is in it, or the source of
-    source_key changed since it was taken."""
+    source_key (one key or a tuple of keys) changed since it was taken."""
     data = load_traffic(md_path)
     if data is None:
         return None
-    src = KERNEL_SOURCES.get(source_key)
-    if src is None or data["sources"].get(source_key) != source_hash(src):
-        return None
+    for key in (source_key,) if isinstance(source_key, str) else source_key:
+        src = KERNEL_SOURCES.get(key)
+        if src is None or data["sources"].get(key) != source_hash(src):
+            return None
     total, found = 0, False
     for frag, idx in kernels:
         for name, d in data["kernels"].items():

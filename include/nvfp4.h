@@ -254,6 +254,53 @@ int mxfp4_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const ui
                int64_t M, int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc,
                hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * FP8, the baseline format (gist.science summary, Resumen técnico §1 and §4:
+ * NVFP4 is measured against an FP8 run; deultimominuto.info, "Cómo funciona
+ * NVFP4": E4M3 has 4 exponent and 3 mantissa bits). One E4M3FN byte per
+ * element (bias 7, largest 448, no infinities) and one float32 decode scale
+ * per tensor: S8 = fp32(amax / 448), replaced by 1 below 2^-100;
+ * r = fp32(1 / S8); y = fp32(x * r); byte = E4M3FN nearest to |y|, ties to
+ * the even mantissa, saturating at 448, with the sign bit of y (so -0.0
+ * gives 0x80). Bytes 0x7F and 0xFF (NaN) are never produced. A non-finite
+ * amax sets *dev_status = 1 (codes unspecified), as for nvfp4_quantize.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * fp8_quantize -- FP8 copies of x [rows][ldx] (NVFP4_F32 or NVFP4_BF16):
+ *   outputs & NVFP4_OUT_ROW: q_row [rows][cols] (row-major bytes);
+ *   outputs & NVFP4_OUT_COL: q_col [cols][rows], the same bytes transposed
+ *     (the K-contiguous operand of the weight-gradient GEMM); needs
+ *     rows % 16 == 0.
+ * cols % 16 == 0, ldx >= cols, every row of x and both outputs 16-byte
+ * aligned. amax_in / amax_ws / tensor_scale / dev_status as for
+ * nvfp4_quantize (amax_ws: NVFP4_AMAX_WS_BYTES of device memory, amax_ws[0]
+ * receives the amax); *tensor_scale receives S8. Two passes over x (amax,
+ * then quantization) unless amax_in is given.
+ */
+int fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int outputs,
+                 const float* amax_in, float* amax_ws, uint8_t* q_row, uint8_t* q_col,
+                 float* tensor_scale, int32_t* dev_status, hipStream_t stream);
+
+/*
+ * fp8_dequantize -- y [rows][ldy] = fp32(e4m3(q) * S8) as float32, or its
+ * round-to-nearest-even bf16, from q [rows][cols]. cols % 16 == 0,
+ * ldy >= cols, 16-byte aligned rows.
+ */
+int fp8_dequantize(const uint8_t* q, const float* tensor_scale, int64_t rows, int64_t cols,
+                   int out_dtype, void* y, int64_t ldy, hipStream_t stream);
+
+/*
+ * fp8_gemm -- C[M][N] = S8_a * S8_b * sum_k e4m3(qa[m][k]) e4m3(qb[n][k]),
+ * both operands K-contiguous ([M][K] and [N][K] bytes, 16-byte aligned),
+ * float32 accumulation on gfx950's FP8 MFMA (products exact), the scales
+ * applied once in the epilogue; C in c_dtype with leading dimension
+ * ldc >= N (element alignment suffices). ta / tb: device float32 decode
+ * scales as fp8_quantize writes them. K % 64 == 0 (K == 0 writes zeros).
+ */
+int fp8_gemm(const uint8_t* qa, const float* ta, const uint8_t* qb, const float* tb, int64_t M,
+             int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,14 +64,17 @@ def fp8_encode(y) -> np.ndarray:
     return (e4m3_encode(np.abs(y)) | sign).astype(np.uint8)
 
 
-def fp8_quantize(x):
-    """F2-F4 for a float32 matrix x [R, C].
+def fp8_quantize(x, amax=None):
+    """F2-F4 for a float32 matrix x [R, C]. ``amax`` is the tensor amax when
+    the caller supplies it (x may then be a slice of the tensor), else the
+    largest magnitude of x.
 
     Returns (row codes [R][C] uint8, column codes [C][R] uint8, S8 float32)."""
     x = np.asarray(x, dtype=np.float32)
     if not np.all(np.isfinite(x)):
         raise ValueError("fp8_quantize: non-finite input")
-    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+    if amax is None:
+        amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
     s8 = fp8_tensor_scale(amax)
     r = np.float32(np.float32(1.0) / s8)
     y = (x * r).astype(np.float32)  # float32 * float32 rounds once

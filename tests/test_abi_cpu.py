@@ -27,7 +27,7 @@ def L():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|uint32_t|const char\*)\s+((?:nvfp4|mxfp4)_\w+)\(",
+    return sorted(set(re.findall(r"^\s*(?:int|uint32_t|const char\*)\s+((?:nvfp4|mxfp4|fp8)_\w+)\(",
                                  text, re.M)))
 
 
@@ -163,6 +163,38 @@ def test_mxfp4_argument_errors(L):
     assert g(qb=None) == 1
     assert g(qa=MIS) == 4
     assert g(N=0) == 0
+
+
+def test_fp8_argument_errors(L):
+    q = lambda **kw: L.fp8_quantize(*dict(dict(x=FAKE, xd=1, rows=32, cols=64, ldx=64, outputs=3,
+                                               amax_in=None, ws=FAKE, q_row=FAKE, q_col=FAKE,
+                                               ts=FAKE, st=None, stream=None), **kw).values())
+    assert q(outputs=0) == 3 and q(outputs=4) == 3
+    assert q(xd=4) == 3
+    assert q(cols=40, ldx=40) == 2      # cols % 16
+    assert q(rows=24) == 2              # the column copy needs rows % 16
+    assert q(ldx=32) == 2
+    assert q(ts=None) == 1
+    assert q(ws=None) == 1
+    assert q(q_col=None) == 1
+    assert q(outputs=1, q_row=None) == 1
+    assert q(q_row=MIS) == 4
+    assert q(x=MIS) == 4
+    d = lambda **kw: L.fp8_dequantize(*dict(dict(q=FAKE, ts=FAKE, rows=32, cols=64, od=0, y=FAKE,
+                                                 ldy=64, st=None), **kw).values())
+    assert d(cols=24, ldy=24) == 2
+    assert d(od=3) == 3
+    assert d(ts=None) == 1
+    assert d(y=MIS) == 4
+    g = lambda **kw: L.fp8_gemm(*dict(dict(qa=FAKE, ta=FAKE, qb=FAKE, tb=FAKE, M=32, N=32, K=64,
+                                           c=FAKE, cd=1, ldc=32, st=None), **kw).values())
+    assert g(K=96) == 2              # K steps of 64
+    assert g(ldc=16) == 2
+    assert g(cd=5) == 3
+    assert g(tb=None) == 1
+    assert g(qb=MIS) == 4
+    assert g(c=FAKE + 1, cd=0) == 4
+    assert g(M=0) == 0
 
 
 def test_hook_argument_errors(L):
