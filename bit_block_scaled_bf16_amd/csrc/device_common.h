@@ -28,15 +28,13 @@ __device__ __forceinline__ float tensor_scale_from_amax(float amax) {
 }
 
 // E4M3FN byte nearest to t (t >= 0, finite), ties to even mantissa,
-// saturating at 448 (0x7E).
+// saturating at 448 (0x7E). gfx950's converter rounds to nearest even into
+// OCP E4M3FN, subnormals included, but gives NaN above 464, hence the clamp
+// (checked against the CPU definition for every float32 near every E4M3
+// value and midpoint).
 __device__ __forceinline__ uint32_t e4m3_from_float(float t) {
-  const uint32_t u = __float_as_uint(t);
-  // t < 2^-6: subnormal grid m * 2^-9 (m == 8 is 2^-6, byte 0x08)
-  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(fminf(t, 0.015625f) * 512.0f));
-  // otherwise keep 3 mantissa bits, round to nearest even, rebias 127 -> 7
-  const uint32_t nrm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
-  const uint32_t v = (u < 0x3C800000u) ? sub : nrm;
-  return (t >= 448.0f) ? 0x7Eu : v;
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(t, 448.0f), 0.0f, 0,
+                                                               false)) & 0xFFu;
 }
 
 // Value of an E4M3FN byte b in 0x00..0x7E, branch-free: b << 20 places the
@@ -46,23 +44,6 @@ __device__ __forceinline__ uint32_t e4m3_from_float(float t) {
 // multiply by 2^120 is exact (float32 subnormals are kept).
 __device__ __forceinline__ float e4m3_to_float(uint32_t b) {
   return __uint_as_float((b & 0x7Fu) << 20) * 0x1p120f;
-}
-
-// Block scale and encode multiplier for a block with amax a_b.
-struct BlockScale {
-  uint32_t byte;  // E4M3 scale byte
-  float mult;     // 1 / (s_f * S), 0 when the scale is 0 (block quantizes to 0)
-};
-
-__device__ __forceinline__ BlockScale block_scale(float amax_b, float six_s, float s) {
-  BlockScale bs;
-  bs.byte = e4m3_from_float(__fdiv_rn(amax_b, six_s));
-  const float sf = e4m3_to_float(bs.byte);
-  // the division always runs (on 1.0 for a zero scale), so no branch
-  const float denom = (bs.byte == 0u) ? 1.0f : __fmul_rn(sf, s);
-  const float r = __fdiv_rn(1.0f, denom);
-  bs.mult = (bs.byte == 0u) ? 0.0f : r;
-  return bs;
 }
 
 // ---------------------------------------------------------------------------
@@ -90,26 +71,46 @@ __device__ __forceinline__ uint32_t pack8_rn(const float* y) {
   return w;
 }
 
-// Stochastically rounded E2M1 code of y from 16 random bits u16: with
+// Stochastic rounding of y to E2M1 from 16 random bits u16: with
 // a = min(|y|, 6), lo the largest magnitude <= a and hi the next one, round
 // up exactly when (a - lo) / (hi - lo) + u16 / 2^16 >= 1.
 //
-// Scaled by 2^-126, the E2M1 grid is float32's own bit layout: 1.0 is the
-// smallest normal, the magnitudes below 1 fall in the subnormal range with
-// its uniform spacing, and each binade above holds two grid points, like one
-// mantissa bit. So with B = a's bits on that scale, B >> 22 is lo's code and
-// the 22 bits below are frac * 2^22, and adding u16 * 2^6 carries into bit
-// 22 exactly when frac + u16 / 2^16 >= 1. For a >= 1, B is a's own bits
-// with the exponent lowered by 126 (exact). For a < 1, B = floor(a * 2^23):
-// the floor drops only bits below 2^-22 of a step, and since u16 * 2^6 is an
-// integer, floor((B + u16 * 2^6) / 2^22) still equals floor(2a + u16 / 2^16).
-__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
-  const uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
-  const float a = fminf(fabsf(y), 6.0f);
-  const uint32_t b_norm = __float_as_uint(a) - (126u << 23);
-  const uint32_t b_sub = static_cast<uint32_t>(__fmul_rn(a, 8388608.0f));  // floor(a * 2^23)
-  const uint32_t b = (a < 1.0f) ? b_sub : b_norm;
-  return ((b + (u16 << 6)) >> 22) | sign;
+// Scaled by 2^-126, the E2M1 grid is float32's own bit layout: 1.0 becomes
+// the smallest normal, the magnitudes below 1 fall in the subnormal range
+// with its uniform spacing, and each binade above holds two grid points,
+// like one mantissa bit. So the bits of z = y * 2^-126 rounded toward zero
+// hold y's sign in bit 31, lo's code from bit 22 up and frac * 2^22 below:
+// exactly for |y| >= 1 (a power-of-two scaling of a normal number), and as
+// floor(|y| * 2^23) for |y| < 1 (toward zero onto the subnormal grid, which
+// drops only bits below 2^-22 of a step). Adding u16 * 2^6 carries into bit
+// 22 exactly when frac + u16 / 2^16 >= 1: u16 * 2^6 has no bits below 2^6,
+// so the bits of frac * 2^22 below 2^6 cannot complete a carry. Clearing the
+// fraction bits and scaling back by 2^126 (exact) gives the chosen grid
+// value with y's sign; the round-to-nearest converter encodes it exactly,
+// and a value past 6 (|y| > 6) lands on 6 through its saturation.
+//
+// The toward-zero multiplies switch the wave's float32 rounding mode (MODE
+// bits 1:0) around eight multiplies in one assembly block and restore round
+// to nearest even, the kernels' mode, before the block ends; s_nop 1 gives
+// the mode write two wait states before the VALU reads it.
+__device__ __forceinline__ void scale_rz8(const float* y, uint32_t (&z)[8]) {
+  asm volatile(
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 3\n\t"
+      "s_nop 1\n\t"
+      "v_mul_f32_e64 %0, %8, %16\n\t"
+      "v_mul_f32_e64 %1, %9, %16\n\t"
+      "v_mul_f32_e64 %2, %10, %16\n\t"
+      "v_mul_f32_e64 %3, %11, %16\n\t"
+      "v_mul_f32_e64 %4, %12, %16\n\t"
+      "v_mul_f32_e64 %5, %13, %16\n\t"
+      "v_mul_f32_e64 %6, %14, %16\n\t"
+      "v_mul_f32_e64 %7, %15, %16\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\t"
+      "s_nop 1"
+      : "=&v"(z[0]), "=&v"(z[1]), "=&v"(z[2]), "=&v"(z[3]), "=&v"(z[4]), "=&v"(z[5]),
+        "=&v"(z[6]), "=&v"(z[7])
+      : "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]), "v"(y[4]), "v"(y[5]), "v"(y[6]), "v"(y[7]),
+        "s"(0x1p-126f));
 }
 
 // ---------------------------------------------------------------------------
@@ -149,16 +150,19 @@ __device__ __forceinline__ U4 sr_words(uint32_t k0, uint32_t k1, uint64_t g, uin
                        U4{static_cast<uint32_t>(g), static_cast<uint32_t>(g >> 32), offset, stream});
 }
 
-// Eight SR codes for y[0..7] from one Philox block.
+// Eight SR codes for y[0..7] from one Philox block (element j in nibble j).
 __device__ __forceinline__ uint32_t pack8_sr(const float* y, U4 w) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  uint32_t out = 0;
+  uint32_t z[8];
+  scale_rz8(y, z);
+  float v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t u16 = (ws[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    out |= e2m1_sr(y[j], u16) << (4 * j);
+    const uint32_t t = (z[j] + (u16 << 6)) & 0xFFC00000u;
+    v[j] = __fmul_rn(__uint_as_float(t), 0x1p126f);
   }
-  return out;
+  return pack8_rn(v);
 }
 
 constexpr uint32_t kStreamRow = 0;

@@ -353,22 +353,55 @@ struct QuantParams {
   int outputs;
 };
 
-// Codes of one 16-value column block (or Hadamard block) as two words.
-template <bool kSR>
-__device__ __forceinline__ void column_block(const float (&col)[16], float six_s, float s,
+// Scale byte and element multiplier of a block with amax a_b: the byte is
+// E4M3(fp32(a_b / 6S)); the multiplier r = fp32(1 / fp32(s_f S)) comes from
+// the workgroup's table of the 127 byte values (0 for the zero byte).
+struct BlockMult {
+  uint32_t byte;
+  float mult;
+};
+
+__device__ __forceinline__ BlockMult block_mult(float amax_b, float six_s, const float* rtab) {
+  BlockMult b;
+  b.byte = e4m3_from_float(__fdiv_rn(amax_b, six_s));
+  b.mult = rtab[b.byte];
+  return b;
+}
+
+// Fills rtab[0..127] (LDS) for tensor scale s; the caller synchronizes.
+__device__ __forceinline__ void fill_recip_table(float* rtab, float s) {
+  const int b = threadIdx.x;
+  if (b < 128) rtab[b] = (b == 0 || b == 127) ? 0.0f : __fdiv_rn(1.0f, __fmul_rn(e4m3_to_float(b), s));
+}
+
+// Largest magnitude of n floats (finite inputs; a NaN is skipped, which only
+// matters where the outputs are unspecified anyway).
+template <int n>
+__device__ __forceinline__ float abs_max(const float* v) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < n; ++i) m = fmaxf(m, fabsf(v[i]));
+  return m;
+}
+
+// Codes of one 16-value column block as two words. With kQuarter the values
+// are the Hadamard butterfly's, which leaves out the final 1/4: the block
+// maximum and the multiplier take the 1/4 instead. Scaling by a power of two
+// commutes with the maximum and with the rounding of y = x * r, so the bits
+// are those of quantizing the scaled values, unless a scaled value or r / 4
+// would be a float32 subnormal.
+template <bool kSR, bool kQuarter>
+__device__ __forceinline__ void column_block(const float (&col)[16], float six_s, const float* rtab,
                                              uint32_t k0, uint32_t k1, uint64_t e0,
                                              uint32_t offset, uint32_t& w0, uint32_t& w1,
                                              uint32_t& sbyte) {
-  uint32_t am = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t b = abs_bits(col[i]);
-    am = (b > am) ? b : am;
-  }
-  const BlockScale bs = block_scale(__uint_as_float(am), six_s, s);
+  float am = abs_max<16>(col);
+  if constexpr (kQuarter) am = __fmul_rn(am, 0.25f);
+  BlockMult bm = block_mult(am, six_s, rtab);
+  if constexpr (kQuarter) bm.mult = __fmul_rn(bm.mult, 0.25f);
   float y[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) y[i] = __fmul_rn(col[i], bs.mult);
+  for (int i = 0; i < 16; ++i) y[i] = __fmul_rn(col[i], bm.mult);
   if constexpr (kSR) {
     const uint64_t g = e0 >> 3;
     w0 = pack8_sr(y, sr_words(k0, k1, g, offset, kStreamCol));
@@ -377,10 +410,10 @@ __device__ __forceinline__ void column_block(const float (&col)[16], float six_s
     w0 = pack8_rn(y);
     w1 = pack8_rn(y + 8);
   }
-  const uint32_t keep = (bs.byte == 0u) ? 0u : 0xFFFFFFFFu;
+  const uint32_t keep = (bm.byte == 0u) ? 0u : 0xFFFFFFFFu;
   w0 &= keep;
   w1 &= keep;
-  sbyte = bs.byte;
+  sbyte = bm.byte;
 }
 
 // One lane's 16 x 8 register tile as loaded (bf16 words or float32 values),
@@ -467,6 +500,7 @@ struct Staging {
 template <typename InT, int kMode, bool kSR, bool kRagged>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   __shared__ __attribute__((aligned(16))) Staging st;
+  __shared__ float rtab[128];
 
   const int64_t rows = p.rows, cols = p.cols;
   const Tile t = locate(rows, cols);
@@ -482,6 +516,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     if (p.amax_out != nullptr) *p.amax_out = amax;
     if (!(amax <= 3.402823466e38f) && p.dev_status != nullptr) *p.dev_status = 1;
   }
+  fill_recip_table(rtab, s);
+  __syncthreads();
   const RhtSigns g = rht_signs(p.sign_mask);
   const bool out_row = (p.outputs & 1) != 0 && kMode != kModeRHT;
   const bool out_col = (p.outputs & 2) != 0 || kMode == kModeRHT;
@@ -496,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
         uint32_t am = cur.absmax_bits();
         const uint32_t other = swap_adjacent_lanes(am);
         am = (other > am) ? other : am;
-        const BlockScale bs = block_scale(__uint_as_float(am), six_s, s);
+        const BlockMult bs = block_mult(__uint_as_float(am), six_s, rtab);
         // codes of a zero-scale tile are 0 (a mask, not a branch)
         const uint32_t keep = (bs.byte == 0u) ? 0u : 0xFFFFFFFFu;
         if ((t.cg & 1) == 0) {
@@ -533,18 +569,15 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             if (!kRagged || i < t.nrows) {
-              uint32_t am = 0;
+              float x8[8];
 #pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                const uint32_t b = abs_bits(cur.get(i, j));
-                am = (b > am) ? b : am;
-              }
-              const uint32_t other = swap_adjacent_lanes(am);
-              am = (other > am) ? other : am;
-              const BlockScale bs = block_scale(__uint_as_float(am), six_s, s);
+              for (int j = 0; j < 8; ++j) x8[j] = cur.get(i, j);
+              const float mine = abs_max<8>(x8);
+              const float am = fmaxf(mine, __uint_as_float(swap_adjacent_lanes(__float_as_uint(mine))));
+              const BlockMult bs = block_mult(am, six_s, rtab);
               float y[8];
 #pragma unroll
-              for (int j = 0; j < 8; ++j) y[j] = __fmul_rn(cur.get(i, j), bs.mult);
+              for (int j = 0; j < 8; ++j) y[j] = __fmul_rn(x8[j], bs.mult);
               uint32_t w;
               if constexpr (kSR) {
                 const uint64_t e = static_cast<uint64_t>(t.r0 + i) * static_cast<uint64_t>(cols) +
@@ -571,8 +604,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
               c1[i] = cur.get(i, 2 * k + 1);
             }
             if constexpr (kMode == kModeRHT) {
-              rht16(c0, g);
-              rht16(c1, g);
+              rht16_unscaled(c0, g);
+              rht16_unscaled(c1, g);
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -580,7 +613,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
               const uint64_t e0 = static_cast<uint64_t>(t.c0 + j) * static_cast<uint64_t>(rows) +
                                   static_cast<uint64_t>(t.r0);
               uint32_t w0, w1, sb;
-              column_block<kSR>(h == 0 ? c0 : c1, six_s, s, p.k0, p.k1, e0, p.offset, w0, w1, sb);
+              column_block<kSR, kMode == kModeRHT>(h == 0 ? c0 : c1, six_s, rtab, p.k0, p.k1, e0,
+                                                   p.offset, w0, w1, sb);
               uint32_t* dst = reinterpret_cast<uint32_t*>(st.codes + (c_local0 + j) * kLdsCodeStride +
                                                           (r_local >> 1));
               dst[0] = w0;
