@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import oracle as o
+from oracle.philox import STREAM_ROW
 import workloads as wl
 from tests._helpers import announce, host, require_gpu, to_device
 
@@ -96,6 +97,70 @@ def test_sr_bit_exact(dtype):
     announce(f"SR {dtype}")
     check_against_oracle(x, dtype, rounding="sr", seed=7, offset=3)
     check_against_oracle(x, dtype, rounding="sr", seed=(1 << 40) + 9, offset=0xFFFFFFFF)
+
+
+def _sr_boundary_matrix(rows, cols, seed, offset, stream):
+    """A float32 matrix whose SR decisions sit on their boundaries.
+
+    The tensor amax is 2688 (S = 1) and every 16-block holds a 6.0, so
+    s_f = 1 and y = x exactly. The other elements are built from the random
+    word u that the oracle's Philox gives their index, with
+    k = 2^16 - u:
+      kind 0: y = (256 k - 1) 2^-25 < 0.5, so frac 2^16 = k - 2^-8 and the
+              element rounds down; rounding y * 2^23 to nearest instead of
+              toward zero would round it up;
+      kind 1: y = k 2^-17, frac 2^16 = k exactly: rounds up;
+      kind 2: y = 1 + k 2^-17 - 2^-23 in [1, 2): rounds down;
+      kind 3: y = 1 + k 2^-17: rounds up;
+      kind 4: y in (6, 6.375]: saturates at 6;
+      kind 5: y = 2^-140 (a float32 subnormal): rounds to 0;
+    each with a random sign. Returns (x, expected magnitude codes, mask of
+    the constructed elements)."""
+    rng = np.random.default_rng(11)
+    e = np.arange(rows * cols, dtype=np.int64).reshape(rows, cols)
+    u = o.sr_random_u16(seed, offset, stream, e).astype(np.int64)
+    k = 65536 - u
+    kind = rng.integers(0, 6, (rows, cols))
+    mag = np.select(
+        [kind == 0, kind == 1, kind == 2, kind == 3, kind == 4],
+        [(256.0 * k - 1.0) * 2.0 ** -25, k * 2.0 ** -17, 1.0 + k * 2.0 ** -17 - 2.0 ** -23,
+         1.0 + k * 2.0 ** -17, rng.uniform(6.0001, 6.375, (rows, cols))],
+        2.0 ** -140)
+    want = np.select(
+        [kind == 0, kind == 1, kind == 2, kind == 3, kind == 4],
+        [np.zeros_like(k), np.where(k == 65536, 1, 1), np.where(k * 2 >= 65536, 2, 2),
+         np.where(1.0 + k * 2.0 ** -17 >= 1.5, 4, 3), np.full_like(k, 7)], 0)
+    # kind 2 stays on its lower grid point: 1.0, or 1.5 when y >= 1.5
+    want = np.where((kind == 2) & (mag >= 1.5), 3, want)
+    # kind 3: the grid point above y (1.5 below 1.5, 2.0 from 1.5 on)
+    want = np.where(kind == 3, np.where(mag >= 1.5, 4, 3), want)
+    x = (mag * np.where(rng.integers(0, 2, (rows, cols)) == 1, -1.0, 1.0)).astype(np.float32)
+    x[:, ::16] = 6.0
+    x[0, 0] = 2688.0
+    built = np.ones((rows, cols), bool)
+    built[:, ::16] = False
+    built[0, :16] = False  # the block holding the tensor amax has another scale
+    return x, want, built
+
+
+def test_sr_decisions_on_their_boundaries():
+    """Row-blocked SR at the exact decision boundaries (see the matrix
+    builder): the kernel's codes equal the oracle's, and both equal the
+    codes the rule prescribes."""
+    torch = require_gpu()
+    import bit_block_scaled_bf16_amd as nv
+
+    rows, cols, seed, offset = 64, 512, 7, 5
+    x, want, built = _sr_boundary_matrix(rows, cols, seed, offset, STREAM_ROW)
+    announce("SR boundary values")
+    ref = o.quantize(x, rounding="sr", seed=seed, offset=offset, outputs=("row",))["row"]
+    ref_codes = o.unpack_codes(ref.codes)
+    assert np.all(ref.scales[1:] == 0x38) and np.all(ref.scales[0, 1:] == 0x38)
+    assert np.array_equal((ref_codes & 7)[built], want[built].astype(np.uint8))
+    row, _, _ = nv.quantize(to_device(x, "fp32"), rounding=nv.ROUND_SR, seed=seed, offset=offset,
+                            outputs=nv.OUT_ROW)
+    assert np.array_equal(host(row.scales), ref.scales)
+    assert np.array_equal(o.unpack_codes(host(row.codes)), ref_codes)
 
 
 def test_caller_supplied_amax():
