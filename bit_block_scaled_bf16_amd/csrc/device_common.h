@@ -85,8 +85,8 @@ __device__ __forceinline__ uint32_t pack8_rn(const float* y) {
 // drops only bits below 2^-22 of a step). Adding u16 * 2^6 carries into bit
 // 22 exactly when frac + u16 / 2^16 >= 1: u16 * 2^6 has no bits below 2^6,
 // so the bits of frac * 2^22 below 2^6 cannot complete a carry. Clearing the
-// fraction bits and scaling back by 2^126 (exact) gives the chosen grid
-// value with y's sign; the round-to-nearest converter encodes it exactly,
+// fraction bits gives the chosen grid value times 2^-126 with y's sign; the
+// round-to-nearest converter, told to scale by 2^126, encodes it exactly,
 // and a value past 6 (|y| > 6) lands on 6 through its saturation.
 //
 // The toward-zero multiplies switch the wave's float32 rounding mode (MODE
@@ -151,6 +151,9 @@ __device__ __forceinline__ U4 sr_words(uint32_t k0, uint32_t k1, uint64_t g, uin
 }
 
 // Eight SR codes for y[0..7] from one Philox block (element j in nibble j).
+// The converter's scale operand acts as a power of two and divides: with
+// scale 2^-126 it encodes the chosen grid value t * 2^126 directly, the
+// subnormal t = 2^-127 (the value 0.5) included.
 __device__ __forceinline__ uint32_t pack8_sr(const float* y, U4 w) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   uint32_t z[8];
@@ -159,10 +162,14 @@ __device__ __forceinline__ uint32_t pack8_sr(const float* y, U4 w) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t u16 = (ws[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    const uint32_t t = (z[j] + (u16 << 6)) & 0xFFC00000u;
-    v[j] = __fmul_rn(__uint_as_float(t), 0x1p126f);
+    v[j] = __uint_as_float((z[j] + (u16 << 6)) & 0xFFC00000u);
   }
-  return pack8_rn(v);
+  uint32_t out = 0;
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[0], v[1], 0x1p-126f, 0);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[2], v[3], 0x1p-126f, 1);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[4], v[5], 0x1p-126f, 2);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[6], v[7], 0x1p-126f, 3);
+  return out;
 }
 
 constexpr uint32_t kStreamRow = 0;
