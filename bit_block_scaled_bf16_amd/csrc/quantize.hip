@@ -675,6 +675,153 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row copy only (1x16 blocks, no column copy): a streaming kernel. Thread
+// (ty = tid / 32, tx = tid % 32) of workgroup (bx, by) owns the 32-value
+// chunk 32 bx + tx of rows 8 by + ty, 8 (by + gridDim.y) + ty, ...: two
+// whole 1x16 blocks in registers (no exchange between lanes), read as one
+// contiguous 64-byte run (bf16), written as 16 bytes of codes and 2 scale
+// bytes. A wave covers 1 KiB of two rows per load instruction, the loads of
+// the next row are in flight while a row is quantized, and the workgroup
+// needs LDS only for the reciprocal table.
+// ---------------------------------------------------------------------------
+constexpr int kRowChunk = 32;    // values per thread and row
+constexpr int kRowGroups = 512;  // most workgroups along the rows
+
+template <typename InT>
+struct Chunk;
+
+template <>
+struct Chunk<uint16_t> {
+  uint4 r[4];
+  __device__ __forceinline__ float get(int j) const {
+    const uint4& v = r[j >> 3];
+    const int k = (j >> 1) & 3;
+    const uint32_t w = k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+};
+
+template <>
+struct Chunk<float> {
+  float4 r[8];
+  __device__ __forceinline__ float get(int j) const {
+    const float4& v = r[j >> 2];
+    return (j & 3) == 0 ? v.x : (j & 3) == 1 ? v.y : (j & 3) == 2 ? v.z : v.w;
+  }
+};
+
+// Loads the chunk's first nblk (1 or 2) blocks; absent blocks read as zero.
+template <typename InT>
+__device__ __forceinline__ void load_chunk(const InT* __restrict__ src, int nblk, Chunk<InT>& c) {
+  constexpr int kPerBlock = 32 / (16 / sizeof(InT)) / 2;  // 16-byte loads per 16 values
+#pragma unroll
+  for (int i = 0; i < 2 * kPerBlock; ++i) {
+    const uint4 v = (i < nblk * kPerBlock) ? reinterpret_cast<const uint4*>(src)[i]
+                                           : make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (sizeof(InT) == 2) {
+      c.r[i] = v;
+    } else {
+      c.r[i] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                           __uint_as_float(v.w));
+    }
+  }
+}
+
+template <typename InT, bool kSR>
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QuantParams p) {
+  __shared__ float rtab[128];
+  __shared__ float amax_lds;
+  const int64_t rows = p.rows, cols = p.cols;
+  const int64_t nblk_row = cols >> 4;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int64_t chunk = static_cast<int64_t>(blockIdx.x) * 32 + tx;
+  const int64_t c0 = chunk * kRowChunk;
+  // blocks of this chunk that exist: 2, 1 (a row of 16 * odd values) or 0
+  const int64_t left = nblk_row - 2 * chunk;
+  const int nblk = left >= 2 ? 2 : (left > 0 ? static_cast<int>(left) : 0);
+  const int64_t row_step = static_cast<int64_t>(gridDim.y) * 8;
+  int64_t row = static_cast<int64_t>(blockIdx.y) * 8 + ty;
+  const InT* x = static_cast<const InT*>(p.x);
+
+  Chunk<InT> cur;
+  if (row < rows) load_chunk<InT>(x + row * p.ldx + c0, nblk, cur);
+  // the tensor amax from the partial maxima: one wave reduces, the others
+  // read it after the barrier that also publishes the reciprocal table
+  if (threadIdx.x < 64) {
+    const float a = p.amax_in != nullptr ? *p.amax_in : reduce_partials(p.partials, p.n_partials);
+    if (threadIdx.x == 0) amax_lds = a;
+  }
+  __syncthreads();
+  const float amax = amax_lds;
+  const float s = tensor_scale_from_amax(amax);
+  const float six_s = __fmul_rn(6.0f, s);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    *p.tensor_scale = s;
+    if (p.amax_out != nullptr) *p.amax_out = amax;
+    if (!(amax <= 3.402823466e38f) && p.dev_status != nullptr) *p.dev_status = 1;
+  }
+  fill_recip_table(rtab, s);
+  __syncthreads();
+  if (nblk == 0) return;  // no barrier below
+
+  // rows of 16 * even values keep 16-byte code and 2-byte scale stores aligned
+  const bool wide_stores = (nblk_row & 1) == 0;
+  for (; row < rows; row += row_step) {
+    Chunk<InT> nxt;
+    const int64_t next = row + row_step;
+    if (next < rows) load_chunk<InT>(x + next * p.ldx + c0, nblk, nxt);
+    uint32_t w[4], sb[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = cur.get(16 * b + j);
+      const BlockMult bm = block_mult(abs_max<16>(v), six_s, rtab);
+      float y[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) y[j] = __fmul_rn(v[j], bm.mult);
+      if constexpr (kSR) {
+        const uint64_t g = (static_cast<uint64_t>(row) * static_cast<uint64_t>(cols) +
+                            static_cast<uint64_t>(c0 + 16 * b)) >> 3;
+        w[2 * b] = pack8_sr(y, sr_words(p.k0, p.k1, g, p.offset, kStreamRow));
+        w[2 * b + 1] = pack8_sr(y + 8, sr_words(p.k0, p.k1, g + 1, p.offset, kStreamRow));
+      } else {
+        w[2 * b] = pack8_rn(y);
+        w[2 * b + 1] = pack8_rn(y + 8);
+      }
+      const uint32_t keep = (bm.byte == 0u) ? 0u : 0xFFFFFFFFu;
+      w[2 * b] &= keep;
+      w[2 * b + 1] &= keep;
+      sb[b] = bm.byte;
+    }
+    uint8_t* qdst = p.q_row + row * (cols >> 1) + c0 / 2;
+    uint8_t* sdst = p.s_row + row * nblk_row + 2 * chunk;
+    if (wide_stores) {
+      *reinterpret_cast<uint4*>(qdst) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint16_t*>(sdst) = static_cast<uint16_t>(sb[0] | (sb[1] << 8));
+    } else {
+      *reinterpret_cast<uint2*>(qdst) = make_uint2(w[0], w[1]);
+      sdst[0] = static_cast<uint8_t>(sb[0]);
+      if (nblk == 2) {
+        *reinterpret_cast<uint2*>(qdst + 8) = make_uint2(w[2], w[3]);
+        sdst[1] = static_cast<uint8_t>(sb[1]);
+      }
+    }
+    cur = nxt;
+  }
+}
+
+template <typename InT, bool kSR>
+void launch_rows(const QuantParams& p, hipStream_t stream) {
+  const int64_t chunks = ((p.cols >> 4) + 1) / 2;
+  const int64_t gx = (chunks + 31) / 32;
+  int64_t gy = (p.rows + 7) / 8;
+  if (gy > kRowGroups) gy = kRowGroups;
+  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+  quantize_rows_kernel<InT, kSR><<<grid, kThreads, 0, stream>>>(p);
+}
+
 template <typename InT, int kMode, bool kSR, bool kRagged>
 void launch_quant(const QuantParams& p, hipStream_t stream) {
   const int64_t tiles =
@@ -714,19 +861,15 @@ int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
   return hipGetLastError() == hipSuccess ? static_cast<int>(g) : -1;
 }
 
-// Ragged row counts (rows % 16 != 0) only reach the 1x16 row-only path: the
-// column copy, 16x16 blocks and the RHT path require rows % 16 == 0.
+// The tile kernel serves every call with a column copy or 16x16 blocks; those
+// require rows % 16 == 0 (ragged row counts reach only the row-copy kernel).
 template <typename InT>
 void dispatch_quant(const QuantParams& p, int mode, bool sr, hipStream_t stream) {
-  const bool ragged = (p.rows % 16) != 0;
   if (mode == kMode2D) {
     launch_quant<InT, kMode2D, false, false>(p, stream);
   } else if (mode == kModeRHT) {
     if (sr) launch_quant<InT, kModeRHT, true, false>(p, stream);
     else launch_quant<InT, kModeRHT, false, false>(p, stream);
-  } else if (ragged) {
-    if (sr) launch_quant<InT, kMode1D, true, true>(p, stream);
-    else launch_quant<InT, kMode1D, false, true>(p, stream);
   } else {
     if (sr) launch_quant<InT, kMode1D, true, false>(p, stream);
     else launch_quant<InT, kMode1D, false, false>(p, stream);
@@ -801,8 +944,20 @@ int launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
   p.sign_mask = q.sign_mask;
   p.outputs = q.outputs;
   const int mode = q.rht ? kModeRHT : (q.block_2d ? kMode2D : kMode1D);
-  if (bf16) dispatch_quant<uint16_t>(p, mode, q.sr, stream);
-  else dispatch_quant<float>(p, mode, q.sr, stream);
+  if (mode == kMode1D && q.outputs == 1) {
+    // the row copy alone streams through its own kernel
+    if (bf16) {
+      if (q.sr) launch_rows<uint16_t, true>(p, stream);
+      else launch_rows<uint16_t, false>(p, stream);
+    } else {
+      if (q.sr) launch_rows<float, true>(p, stream);
+      else launch_rows<float, false>(p, stream);
+    }
+  } else if (bf16) {
+    dispatch_quant<uint16_t>(p, mode, q.sr, stream);
+  } else {
+    dispatch_quant<float>(p, mode, q.sr, stream);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
