@@ -61,6 +61,9 @@ CALL_KERNELS = {
     "quantize_dy_1x16_sr": (("amax_flat_kernel<unsigned short>", 2),
                             ("quantize_kernel<unsigned short, 0, true, false>", 0)),
     "gemm_dgrad": (("gemm_kernel<4, false, true,", 1), ("gemm_kernel<2, false, true,", 1)),
+    # X's weight-gradient copy with SR instead of RN (a variant, after the step)
+    "rht_quantize_x_sr": (("amax_tile_kernel<unsigned short, true, false>", 2),
+                          ("quantize_kernel<unsigned short, 2, true, false>", 1)),
     "mx_quantize_x": (("mx_quantize_kernel<unsigned short>", 0),),
     "mx_quantize_w": (("mx_quantize_kernel<unsigned short>", 1),),
     "mx_gemm_fprop": (("block_gemm_kernel<(Fmt)0", 0),),
@@ -179,6 +182,17 @@ class Step:
                 s.f, s.dx)),
         ]
 
+    def variant_calls(self):
+        """X's RHT copy with SR (the recipe rounds activations to nearest; the
+        library offers both), timed apart from the step into the step's own
+        X-copy buffers after the step's GEMMs have read them."""
+        nv = self.nv
+        s = self
+        return [
+            ("rht_quantize_x_sr", lambda: nv.nvfp4_rht_quantize(
+                s.x, 7, nv.ROUND_SR, 7, s.offset, None, s.axt, s.qxt, s.sxt, s.txt, s.status)),
+        ]
+
     def mx_calls(self):
         """The MXFP4 comparison path, timed apart from the step."""
         nv = self.nv
@@ -218,6 +232,7 @@ class Step:
             "gemm_fprop": ("TFLOP/s", 2.0 * t * f * h),
             "gemm_wgrad": ("TFLOP/s", 2.0 * f * h * t),
             "quantize_dy_1x16_sr": ("GB/s", t * f * (2 + 2 + q1)),
+            "rht_quantize_x_sr": ("GB/s", t * h * (2 + 2 + q1)),
             "gemm_dgrad": ("TFLOP/s", 2.0 * t * h * f),
             # MXFP4: one pass (no tensor amax): bf16 in, codes + 1/32 scale bytes out
             "mx_quantize_x": ("GB/s", t * h * (2 + 0.5 + 1.0 / 32)),
@@ -324,7 +339,8 @@ def main():
     assert int(step.status.cpu()[0]) == 0, "non-finite amax"
 
     # the dgrad path, after the timed step and outside it
-    next_calls = [] if args.no_next else step.next_calls() + step.mx_calls() + step.fp8_calls()
+    next_calls = [] if args.no_next else (step.next_calls() + step.variant_calls() + step.mx_calls()
+                                          + step.fp8_calls())
     for _ in range(min(args.warmup, 1)):
         for _, fn in next_calls:
             fn()
@@ -410,7 +426,8 @@ def main():
                  "us": round(g_us, 1)},
         "kernels": kernels,
         "next": ({"dgrad": {k: v for k, v in next_rows.items()
-                            if not k.startswith("mx_") and not k.startswith("fp8_")},
+                            if k in ("quantize_dy_1x16_sr", "gemm_dgrad")},
+                  "variants": {k: v for k, v in next_rows.items() if k == "rht_quantize_x_sr"},
                   "mxfp4": {k: v for k, v in next_rows.items() if k.startswith("mx_")},
                   "fp8": {k: v for k, v in next_rows.items() if k.startswith("fp8_")}}
                  if next_rows else None),

@@ -5,6 +5,7 @@ Usage (after the rocprofv3 runs that bench.py's docstring lists):
   python -m bit_block_scaled_bf16_amd.profiling stats  <kernel_stats.csv> <out.md> <command>
   python -m bit_block_scaled_bf16_amd.profiling traffic <fetch_dir> <write_dir> <copy_bytes> \
         <out.md> <command>
+  python -m bit_block_scaled_bf16_amd.profiling counters <pmc_dir> <out.md> <command>
 
 `stats` condenses a --kernel-trace --stats CSV into a table of average kernel
 durations. `traffic` turns two --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB
@@ -13,7 +14,8 @@ reads for a copy-like kernel of known size (torch's elementwise bitwise_not,
 which reads and writes the same number of bytes, run by bench.py
 --copy-calibration-mib). The traffic summary carries the SHA-256 of
 each kernel source it covers; bench.py reports the figure only while the
-source is unchanged.
+source is unchanged. `counters` turns one --pmc run of COUNTERS into per-
+dispatch clock, MFMA and VALU busy fractions and instructions per wave.
 """
 
 from __future__ import annotations
@@ -100,6 +102,70 @@ def _per_dispatch(run_dir: str, counter: str):
         agg[d] += float(r["Counter_Value"])
         names[d] = r["Kernel_Name"]
     return [(d, names[d], agg[d]) for d in sorted(agg)]
+
+
+# One --pmc pass (6 SQ counters and 1 GRBM counter, within one pass's limits).
+COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
+            "SQ_INSTS_VALU", "SQ_INSTS_MFMA")
+# MI355X: 256 CUs x 4 SIMDs; GRBM_GUI_ACTIVE is summed over the 8 XCDs.
+SIMDS = 1024
+XCDS = 8
+
+
+def counters_summary(run_dir: str, out_md: str, command: str) -> None:
+    """Per dispatch: duration, average clock (GUI-active cycles / duration),
+    the fraction of SIMD-cycles with an MFMA busy, the fraction with a VALU
+    instruction active (SQ_ACTIVE_INST_VALU counts in units of 4 cycles, the
+    issue time of a wave64 VALU instruction), and VALU / MFMA instructions
+    per wave."""
+    path = None
+    for root, _, files in os.walk(run_dir):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                path = os.path.join(root, fn)
+    if path is None:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    agg = collections.defaultdict(lambda: collections.defaultdict(float))
+    meta = {}
+    for r in csv.DictReader(open(path)):
+        d = int(r["Dispatch_Id"])
+        agg[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        meta[d] = (short_name(r["Kernel_Name"]),
+                   (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [
+        "# Busy fractions per dispatch (rocprofv3 --pmc)",
+        "",
+        f"Command: `{command}`",
+        "",
+        f"Counters (one pass): {' '.join(COUNTERS)}. clock = GRBM_GUI_ACTIVE / {XCDS} / "
+        f"duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({SIMDS} SIMDs x GUI cycles); "
+        f"VALU busy = 4 x SQ_ACTIVE_INST_VALU / ({SIMDS} x GUI cycles). MFMA busy x clock / "
+        "2.4 GHz is the share of the chip's dense MFMA peak that the busy cycles represent. "
+        "The counters cover a window slightly longer than the dispatch, so clock and busy "
+        "fractions of dispatches shorter than about 100 us are approximate (a clock above "
+        "2.4 GHz marks them).",
+        "",
+        "| dispatch | kernel | us | clock GHz | MFMA busy | MFMA busy x clk/2.4 | VALU busy | "
+        "VALU inst/wave | MFMA inst/wave |",
+        "|---|---|---|---|---|---|---|---|---|",
+    ]
+    for d in sorted(agg):
+        name, us = meta[d]
+        if "Fill" in name or "copyBuffer" in name or CALIBRATION_KERNEL in name:
+            continue
+        c = agg[d]
+        gui = c["GRBM_GUI_ACTIVE"] / XCDS
+        if gui <= 0 or us <= 0:
+            continue
+        clk = gui / (us * 1e3)
+        mfma = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * gui)
+        valu = 4.0 * c["SQ_ACTIVE_INST_VALU"] / (SIMDS * gui)
+        waves = max(c["SQ_WAVES"], 1.0)
+        lines.append(f"| {d} | `{name}` | {us:.1f} | {clk:.2f} | {mfma:.3f} | {mfma * clk / 2.4:.3f} | "
+                     f"{valu:.2f} | {c['SQ_INSTS_VALU'] / waves:.0f} | "
+                     f"{c['SQ_INSTS_MFMA'] / waves:.0f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def traffic_summary(fetch_dir: str, write_dir: str, copy_bytes: int, out_md: str,
@@ -194,6 +260,8 @@ def kernel_traffic(md_path: str, kernels, source_key):
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats_summary(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "counters":
+        counters_summary(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
         r = traffic_summary(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5], sys.argv[6])
         print(json.dumps({k: v for k, v in r.items() if k != "kernels"}, indent=1))

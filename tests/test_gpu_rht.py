@@ -103,15 +103,16 @@ def test_end_to_end_against_oracle(rounding):
     assert sb_diff <= 1e-5
 
 
-def test_full_gradient_sr_sampled():
-    """bf16 dY 8192x20480 Laplace(0, 1e-3), RHT (seed 7) + SR (Philox seed 7):
-    transformed values and codes checked on sampled columns."""
+def _full_rht_sampled(x, rounding, seed):
+    """RHT (seed 7) + RN or SR (Philox seed `seed`) of a full-size bf16 tensor:
+    the tensor amax, the transformed values of 32 sampled columns, and their
+    scale bytes and codes (the oracle quantizing the kernel's own transformed
+    values, with the element indices of the full tensor)."""
     torch = require_gpu()
     import bit_block_scaled_bf16_amd as nv
 
-    x = wl.gradient()
-    announce("full gradient 8192x20480 RHT+SR")
-    q, ws = run_rht_quantize(x, "bf16", 1, seed=wl.SR_SEED, offset=0, rht_seed=wl.RHT_SEED)
+    q, ws = run_rht_quantize(x, "bf16", 1 if rounding == "sr" else 0, seed=seed, offset=0,
+                             rht_seed=wl.RHT_SEED)
     xt_full = o.rht(x, wl.RHT_SEED)
     a = np.float32(np.max(np.abs(xt_full)))
     assert abs(float(host(ws)[0]) - float(a)) <= 1e-6 * float(a)
@@ -123,11 +124,25 @@ def test_full_gradient_sr_sampled():
     nv.nvfp4_rht_transform(xg, wl.RHT_SEED, out)
     xt_gpu = host(out)
     assert_transform_close(xt_gpu, xt_full[:, cols])
-    # quantize the sampled columns with the oracle, element indices of the full tensor
     t = x.shape[0]
     sub = np.ascontiguousarray(xt_gpu.T)  # [32, T]
     for i, c in enumerate(cols):
-        codes, sb = o.quantize_rows(sub[i:i + 1], s, "sr", seed=wl.SR_SEED, offset=0, stream=1,
+        codes, sb = o.quantize_rows(sub[i:i + 1], s, rounding, seed=seed, offset=0, stream=1,
                                     index_base=int(c) * t)
         assert np.array_equal(host(q.scales[c:c + 1]), sb), int(c)
         assert np.array_equal(host(q.codes[c:c + 1]), o.pack_codes(codes)), int(c)
+
+
+def test_full_gradient_sr_sampled():
+    """bf16 dY 8192x20480 Laplace(0, 1e-3), RHT (seed 7) + SR (Philox seed 7):
+    transformed values and codes checked on sampled columns."""
+    announce("full gradient 8192x20480 RHT+SR")
+    _full_rht_sampled(wl.gradient(), "sr", wl.SR_SEED)
+
+
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+def test_full_wgrad_activation_sampled(rounding):
+    """The other weight-gradient operand: bf16 X 8192x5120 N(0,1), RHT with
+    the same signs, RN (the recipe's choice for activations) and SR."""
+    announce(f"full wgrad activation 8192x5120 RHT+{rounding}")
+    _full_rht_sampled(wl.wgrad_activation(), rounding, wl.SR_SEED)
