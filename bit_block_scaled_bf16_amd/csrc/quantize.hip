@@ -9,6 +9,11 @@
 // Bidimensional (2D) y Redondeo Estocástico" (16x16 weight tiles; stochastic
 // rounding of gradients).
 //
+// Two quantize kernels. A call that asks for the 1x16 row copy alone goes
+// through quantize_rows_kernel (see its comment), which streams rows. Every
+// other call (a column copy, both copies, 16x16 blocks, the Hadamard path)
+// goes through quantize_kernel, whose decomposition follows.
+//
 // Work decomposition. A workgroup of 256 threads (4 waves) owns a tile of
 // 256 rows x 128 columns. Lane l of wave w owns the 16 rows starting at
 // 64w + 16(l / 16) and the 8 columns starting at 8(l % 16): 16 loads of
@@ -466,16 +471,16 @@ struct RawTile<float> {
   }
 };
 
-// Loads this lane's 16 x 8 values. Lanes past the matrix, and with kRagged
-// the rows at or beyond r0 + nrows (a row count that is not a multiple of 16,
-// allowed only for the row-blocked copy), read as zero.
-template <typename InT, bool kRagged>
+// Loads this lane's 16 x 8 values (lanes past the matrix read zeros). Every
+// call reaching the tile kernel has rows % 16 == 0, so a lane's 16 rows all
+// exist or none does.
+template <typename InT>
 __device__ __forceinline__ void load_raw(const InT* __restrict__ x, int64_t ldx, const Tile& t,
                                          RawTile<InT>& raw) {
   const InT* row = x + t.r0 * ldx + t.c0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const bool ok = t.valid && (!kRagged || i < t.nrows);
+    const bool ok = t.valid;
     if constexpr (sizeof(InT) == 2) {
       raw.r[i] = ok ? *reinterpret_cast<const uint4*>(row) : make_uint4(0u, 0u, 0u, 0u);
     } else {
@@ -497,7 +502,7 @@ struct Staging {
 };
 
 // One workgroup per 256 x 128 tile.
-template <typename InT, int kMode, bool kSR, bool kRagged>
+template <typename InT, int kMode, bool kSR>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   __shared__ __attribute__((aligned(16))) Staging st;
   __shared__ float rtab[128];
@@ -507,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   // the tile's loads go out first; the amax (a few more loads) is reduced
   // while they are in flight
   RawTile<InT> cur;
-  load_raw<InT, kRagged>(static_cast<const InT*>(p.x), p.ldx, t, cur);
+  load_raw<InT>(static_cast<const InT*>(p.x), p.ldx, t, cur);
   const float amax = p.amax_in != nullptr ? *p.amax_in : reduce_partials(p.partials, p.n_partials);
   const float s = tensor_scale_from_amax(amax);
   const float six_s = __fmul_rn(6.0f, s);
@@ -563,33 +568,29 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
         }
       } else {
         if (out_row) {
-          // 1x16 blocks along the row: this lane's 8 values + lane ^ 1's 8.
-          // Rows past a ragged end are skipped by a predicate (the same for
-          // both lanes of a pair), not a loop exit.
+          // 1x16 blocks along the row: this lane's 8 values + lane ^ 1's 8
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            if (!kRagged || i < t.nrows) {
-              float x8[8];
+            float x8[8];
 #pragma unroll
-              for (int j = 0; j < 8; ++j) x8[j] = cur.get(i, j);
-              const float mine = abs_max<8>(x8);
-              const float am = fmaxf(mine, __uint_as_float(swap_adjacent_lanes(__float_as_uint(mine))));
-              const BlockMult bs = block_mult(am, six_s, rtab);
-              float y[8];
+            for (int j = 0; j < 8; ++j) x8[j] = cur.get(i, j);
+            const float mine = abs_max<8>(x8);
+            const float am = fmaxf(mine, __uint_as_float(swap_adjacent_lanes(__float_as_uint(mine))));
+            const BlockMult bs = block_mult(am, six_s, rtab);
+            float y[8];
 #pragma unroll
-              for (int j = 0; j < 8; ++j) y[j] = __fmul_rn(x8[j], bs.mult);
-              uint32_t w;
-              if constexpr (kSR) {
-                const uint64_t e = static_cast<uint64_t>(t.r0 + i) * static_cast<uint64_t>(cols) +
-                                   static_cast<uint64_t>(t.c0);
-                w = pack8_sr(y, sr_words(p.k0, p.k1, e >> 3, p.offset, kStreamRow));
-              } else {
-                w = pack8_rn(y);
-              }
-              w &= (bs.byte == 0u) ? 0u : 0xFFFFFFFFu;
-              *reinterpret_cast<uint32_t*>(p.q_row + (t.r0 + i) * (cols >> 1) + (t.c0 >> 1)) = w;
-              if ((t.cg & 1) == 0) st.row_scales[(r_local + i) * 8 + (t.cg >> 1)] = static_cast<uint8_t>(bs.byte);
+            for (int j = 0; j < 8; ++j) y[j] = __fmul_rn(x8[j], bs.mult);
+            uint32_t w;
+            if constexpr (kSR) {
+              const uint64_t e = static_cast<uint64_t>(t.r0 + i) * static_cast<uint64_t>(cols) +
+                                 static_cast<uint64_t>(t.c0);
+              w = pack8_sr(y, sr_words(p.k0, p.k1, e >> 3, p.offset, kStreamRow));
+            } else {
+              w = pack8_rn(y);
             }
+            w &= (bs.byte == 0u) ? 0u : 0xFFFFFFFFu;
+            *reinterpret_cast<uint32_t*>(p.q_row + (t.r0 + i) * (cols >> 1) + (t.c0 >> 1)) = w;
+            if ((t.cg & 1) == 0) st.row_scales[(r_local + i) * 8 + (t.cg >> 1)] = static_cast<uint8_t>(bs.byte);
           }
         }
         if (out_col) {
@@ -822,11 +823,11 @@ void launch_rows(const QuantParams& p, hipStream_t stream) {
   quantize_rows_kernel<InT, kSR><<<grid, kThreads, 0, stream>>>(p);
 }
 
-template <typename InT, int kMode, bool kSR, bool kRagged>
+template <typename InT, int kMode, bool kSR>
 void launch_quant(const QuantParams& p, hipStream_t stream) {
   const int64_t tiles =
       ((p.rows + kTileRows - 1) / kTileRows) * ((p.cols + kTileCols - 1) / kTileCols);
-  quantize_kernel<InT, kMode, kSR, kRagged><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(p);
+  quantize_kernel<InT, kMode, kSR><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(p);
 }
 
 // Launches the amax kernel for x; returns the number of partial maxima it
@@ -866,13 +867,13 @@ int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
 template <typename InT>
 void dispatch_quant(const QuantParams& p, int mode, bool sr, hipStream_t stream) {
   if (mode == kMode2D) {
-    launch_quant<InT, kMode2D, false, false>(p, stream);
+    launch_quant<InT, kMode2D, false>(p, stream);
   } else if (mode == kModeRHT) {
-    if (sr) launch_quant<InT, kModeRHT, true, false>(p, stream);
-    else launch_quant<InT, kModeRHT, false, false>(p, stream);
+    if (sr) launch_quant<InT, kModeRHT, true>(p, stream);
+    else launch_quant<InT, kModeRHT, false>(p, stream);
   } else {
-    if (sr) launch_quant<InT, kMode1D, true, false>(p, stream);
-    else launch_quant<InT, kMode1D, false, false>(p, stream);
+    if (sr) launch_quant<InT, kMode1D, true>(p, stream);
+    else launch_quant<InT, kMode1D, false>(p, stream);
   }
 }
 
