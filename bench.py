@@ -287,7 +287,20 @@ def cpu_baseline():
                   f"flops / step time",
         "seconds": dt,
         "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
     }
+
+
+def _cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
