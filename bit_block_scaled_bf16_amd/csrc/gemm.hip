@@ -220,23 +220,29 @@ __device__ __forceinline__ void dma_stage(const DmaSource<kT>& d, const uint8_t*
 // Fragments.
 // ---------------------------------------------------------------------------
 
-// An E4M3 scale byte b as fp16 bits b << 7 is exactly value(b) / 256: the
-// exponent and mantissa fields line up with fp16's, and subnormal bytes
-// become fp16 subnormals m * 2^-17 = (m * 2^-9) / 256.
-__device__ __forceinline__ _Float16 scale_f16_div256(uint32_t byte) {
-  return __builtin_bit_cast(_Float16, static_cast<uint16_t>((byte & 0x7Fu) << 7));
+// The block scale of sub-step kk as fp16: byte kk >> 1 of the lane's scale
+// word. gfx950's FP8 (E4M3) -> fp16 converter decodes two bytes per
+// instruction, exactly (every E4M3 value, subnormals included, is an fp16
+// normal number; checked for all 256 bytes). With kk known at compile time
+// the selects fold away and the two conversions of a word are shared by its
+// eight sub-steps.
+__device__ __forceinline__ _Float16 scale_f16(uint32_t w, int kk) {
+  const half2_t p01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const half2_t p23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  const int q = kk >> 1;
+  return q == 0 ? p01[0] : q == 1 ? p01[1] : q == 2 ? p23[0] : p23[1];
 }
 
-// Eight codes (one dword) times a block scale as one MFMA fragment. The
-// converter multiplies each E2M1 value by 2^8 (its scale operand acts as a
-// power of two), so (e2m1 * 256) * (s_f / 256) = e2m1 * s_f: every factor
-// and the product are exact in fp16.
+// Eight codes (one dword) times a block scale as one MFMA fragment: the
+// FP4 converter gives the E2M1 values (scale 1), one packed multiply per
+// pair applies s_f. Every factor and the product (at most 6 significant
+// bits, in [2^-10, 2688]) are exact in fp16.
 __device__ __forceinline__ half8_t expand8(uint32_t w, _Float16 sf) {
   const half2_t s2 = {sf, sf};
-  const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s2;
-  const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s2;
-  const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s2;
-  const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * s2;
+  const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
   return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
@@ -300,8 +306,8 @@ __device__ __forceinline__ void expand_substep(half8_t (&af)[kT], half8_t (&bf)[
                                                const Codes<kT>& c, const Scales<kT>& sc, int kk) {
 #pragma unroll
   for (int i = 0; i < kT; ++i) {
-    af[i] = expand8(dword_of(c.a[i], kk), scale_f16_div256(sc.a[i] >> (8 * (kk >> 1))));
-    bf[i] = expand8(dword_of(c.b[i], kk), scale_f16_div256(sc.b[i] >> (8 * (kk >> 1))));
+    af[i] = expand8(dword_of(c.a[i], kk), scale_f16(sc.a[i], kk));
+    bf[i] = expand8(dword_of(c.b[i], kk), scale_f16(sc.b[i], kk));
   }
 }
 
