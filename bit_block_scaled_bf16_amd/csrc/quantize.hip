@@ -36,7 +36,16 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTileRows = 256;
 constexpr int kTileCols = 128;
-constexpr int kLdsCodeStride = kTileRows / 2 + 8;  // bytes per staged column (+8 pad)
+constexpr int kLdsCodeStride = kTileRows / 2;  // bytes per staged column
+
+// LDS byte offset of byte `byte` of staged column `col` (tile-local). The
+// 16-byte granules of a column are XOR-swizzled by (col >> 3) & 7: the
+// lanes that stage the same rows of 16 different columns then spread over
+// 8 granules (2-way bank conflicts instead of 8-way with a padded row), and a
+// granule stays 16-byte aligned for the write-out.
+__device__ __forceinline__ int staged_code_offset(int col, int byte) {
+  return col * kLdsCodeStride + ((((byte >> 4) ^ ((col >> 3) & 7)) << 4) | (byte & 15));
+}
 constexpr int64_t kMaxTileBlocks = 512;  // workgroups of the tile-shaped amax kernel
 
 enum Mode { kMode1D = 0, kMode2D = 1, kModeRHT = 2 };
@@ -560,8 +569,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
             float col[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) col[i] = __fmul_rn(cur.get(i, j), bs.mult);
-            uint32_t* dst = reinterpret_cast<uint32_t*>(st.codes + (c_local0 + j) * kLdsCodeStride +
-                                                        (r_local >> 1));
+            uint32_t* dst = reinterpret_cast<uint32_t*>(st.codes +
+                                                        staged_code_offset(c_local0 + j, r_local >> 1));
             dst[0] = pack8_rn(col) & keep;
             dst[1] = pack8_rn(col + 8) & keep;
           }
@@ -616,8 +625,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
               uint32_t w0, w1, sb;
               column_block<kSR, kMode == kModeRHT>(h == 0 ? c0 : c1, six_s, rtab, p.k0, p.k1, e0,
                                                    p.offset, w0, w1, sb);
-              uint32_t* dst = reinterpret_cast<uint32_t*>(st.codes + (c_local0 + j) * kLdsCodeStride +
-                                                          (r_local >> 1));
+              uint32_t* dst = reinterpret_cast<uint32_t*>(
+                  st.codes + staged_code_offset(c_local0 + j, r_local >> 1));
               dst[0] = w0;
               dst[1] = w1;
               st.col_scales[(c_local0 + j) * 16 + (r_local >> 4)] = static_cast<uint8_t>(sb);
@@ -645,18 +654,32 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
       }
     }
     if (out_col) {
-      // each column's codes for this tile's rows are contiguous in q_col; 16
-      // lanes write one column's 128 bytes, and its 16 scale bytes (1D) leave
-      // as one store where alignment allows
+      // each column's codes for this tile's rows are contiguous in q_col: 8
+      // lanes write one column's 128 bytes as 16-byte granules (8-byte chunks
+      // when rows % 32 != 0 leaves column starts only 8-byte aligned), and its
+      // 16 scale bytes (1D) leave as one store where alignment allows
       const int64_t rows_here = (rows - tr * kTileRows) < kTileRows ? (rows - tr * kTileRows) : kTileRows;
       const int code_chunks = static_cast<int>(rows_here >> 4);  // 8-byte chunks per column
+      if ((rows & 31) == 0) {
+        const int granules = code_chunks >> 1;
 #pragma unroll
-      for (int k = tid; k < kTileCols * (kTileRows / 16); k += kThreads) {
-        const int c_local = k >> 4, ch = k & 15;
-        const int64_t col = tc * kTileCols + c_local;
-        if (col < cols && ch < code_chunks) {
-          const uint2 val = *reinterpret_cast<const uint2*>(st.codes + c_local * kLdsCodeStride + ch * 8);
-          *reinterpret_cast<uint2*>(p.q_col + col * (rows >> 1) + tr * (kTileRows / 2) + ch * 8) = val;
+        for (int k = tid; k < kTileCols * (kTileRows / 32); k += kThreads) {
+          const int c_local = k >> 3, g = k & 7;
+          const int64_t col = tc * kTileCols + c_local;
+          if (col < cols && g < granules) {
+            const uint4 val = *reinterpret_cast<const uint4*>(st.codes + staged_code_offset(c_local, 16 * g));
+            *reinterpret_cast<uint4*>(p.q_col + col * (rows >> 1) + tr * (kTileRows / 2) + 16 * g) = val;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = tid; k < kTileCols * (kTileRows / 16); k += kThreads) {
+          const int c_local = k >> 4, ch = k & 15;
+          const int64_t col = tc * kTileCols + c_local;
+          if (col < cols && ch < code_chunks) {
+            const uint2 val = *reinterpret_cast<const uint2*>(st.codes + staged_code_offset(c_local, 8 * ch));
+            *reinterpret_cast<uint2*>(p.q_col + col * (rows >> 1) + tr * (kTileRows / 2) + ch * 8) = val;
+          }
         }
       }
       if constexpr (kMode != kMode2D) {
