@@ -5,12 +5,16 @@ Workload (synthetic stand-ins for a linear layer of the 12B hybrid model of
 N(0,1) with 16 outlier channels x20, W bf16 [20480, 5120] N(0, 0.02^2),
 dY bf16 [16384, 20480] Laplace(0, 1e-3). One step runs the whole hot path:
 
-  1. nvfp4_quantize(X)        tensor amax + 1x16 RN, row copy  (fprop A)
-  2. nvfp4_quantize(W)        tensor amax + 16x16 RN, W and W^T (fprop B)
-  3. nvfp4_rht_quantize(dY)   RHT amax + RHT + 16x1 SR (Philox seed 7)
-  4. nvfp4_rht_quantize(X)    RHT amax + RHT + 16x1 RN
-  5. nvfp4_gemm fprop         Y  [16384, 20480] = X W^T,  K = 5120,  bf16
-  6. nvfp4_gemm wgrad         dW [20480, 5120] = dY^T X,  K = 16384, bf16
+  1. nvfp4_quantize_row_rht(X)  both amaxes, then in one read: 1x16 RN row
+                                copy (fprop A) and RHT + 16x1 RN (wgrad B)
+  2. nvfp4_quantize(W)          tensor amax + 16x16 RN, W and W^T (fprop B)
+  3. nvfp4_rht_quantize(dY)     RHT amax + RHT + 16x1 SR (Philox seed 7)
+  4. nvfp4_gemm fprop           Y  [16384, 20480] = X W^T,  K = 5120,  bf16
+  5. nvfp4_gemm wgrad           dW [20480, 5120] = dY^T X,  K = 16384, bf16
+
+X's two copies are also timed as separate calls (nvfp4_quantize row copy,
+nvfp4_rht_quantize RN) after the step, with the dgrad path and the
+MXFP4 / FP8 comparisons.
 
 Prints one JSON line. `value` is the step's effective GEMM rate: the two
 GEMMs' 2*M*N*K flops divided by the whole step time (quantizers included).
@@ -47,23 +51,25 @@ TRAFFIC_SUMMARY = "linear_layer_traffic.md"
 # quantize kernel; a GEMM call launches 256 x 256 tiles and, for a last
 # partial round, 128 x 128 ones.
 CALL_KERNELS = {
-    "quantize_x_1x16": (("amax_flat_kernel<unsigned short>", 0),
-                        ("quantize_kernel<unsigned short, 0, false, false>", 0)),
-    "quantize_w_16x16": (("amax_flat_kernel<unsigned short>", 1),
-                         ("quantize_kernel<unsigned short, 1, false, false>", 0)),
-    "rht_quantize_dy_sr": (("amax_tile_kernel<unsigned short, true, false>", 0),
-                           ("quantize_kernel<unsigned short, 2, true, false>", 0)),
-    "rht_quantize_x_rn": (("amax_tile_kernel<unsigned short, true, false>", 1),
-                          ("quantize_kernel<unsigned short, 2, false, false>", 0)),
+    "quantize_x_row_rht": (("amax_tile_kernel<unsigned short, true, false, true>", 0),
+                           ("quantize_kernel<unsigned short, 3, false>", 0)),
+    "quantize_w_16x16": (("amax_flat_kernel<unsigned short>", 0),
+                         ("quantize_kernel<unsigned short, 1, false>", 0)),
+    "rht_quantize_dy_sr": (("amax_tile_kernel<unsigned short, true, false, false>", 0),
+                           ("quantize_kernel<unsigned short, 2, true>", 0)),
     "gemm_fprop": (("gemm_kernel<4, false, true,", 0), ("gemm_kernel<2, false, true,", 0)),
     "gemm_wgrad": (("gemm_kernel<4, false, false,", 0), ("gemm_kernel<2, false, false,", 0)),
     # the dgrad path, run after the step
-    "quantize_dy_1x16_sr": (("amax_flat_kernel<unsigned short>", 2),
-                            ("quantize_kernel<unsigned short, 0, true, false>", 0)),
+    "quantize_dy_1x16_sr": (("amax_flat_kernel<unsigned short>", 1),
+                            ("quantize_rows_kernel<unsigned short, true>", 0)),
     "gemm_dgrad": (("gemm_kernel<4, false, true,", 1), ("gemm_kernel<2, false, true,", 1)),
-    # X's weight-gradient copy with SR instead of RN (a variant, after the step)
-    "rht_quantize_x_sr": (("amax_tile_kernel<unsigned short, true, false>", 2),
-                          ("quantize_kernel<unsigned short, 2, true, false>", 1)),
+    # X's two copies as separate calls, and its RHT copy with SR (after the step)
+    "quantize_x_1x16": (("amax_flat_kernel<unsigned short>", 2),
+                        ("quantize_rows_kernel<unsigned short, false>", 0)),
+    "rht_quantize_x_rn": (("amax_tile_kernel<unsigned short, true, false, false>", 1),
+                          ("quantize_kernel<unsigned short, 2, false>", 0)),
+    "rht_quantize_x_sr": (("amax_tile_kernel<unsigned short, true, false, false>", 2),
+                          ("quantize_kernel<unsigned short, 2, true>", 1)),
     "mx_quantize_x": (("mx_quantize_kernel<unsigned short>", 0),),
     "mx_quantize_w": (("mx_quantize_kernel<unsigned short>", 1),),
     "mx_gemm_fprop": (("block_gemm_kernel<(Fmt)0", 0),),
@@ -150,16 +156,14 @@ class Step:
         nv = self.nv
         s = self
         return [
-            ("quantize_x_1x16", lambda: nv.nvfp4_quantize(
-                s.x, nv.BLOCK_1D, nv.ROUND_RN, 0, 0, nv.OUT_ROW, None, s.ax, s.qx, s.sx, None,
-                None, s.tx, s.status)),
+            ("quantize_x_row_rht", lambda: nv.nvfp4_quantize_row_rht(
+                s.x, 7, nv.ROUND_RN, 0, 0, None, s.ax, s.qx, s.sx, s.tx, s.qxt, s.sxt, s.txt,
+                s.status)),
             ("quantize_w_16x16", lambda: nv.nvfp4_quantize(
                 s.w, nv.BLOCK_2D, nv.ROUND_RN, 0, 0, nv.OUT_ROW | nv.OUT_COL, None, s.aw, s.qw,
                 s.sw, s.qwt, s.swt, s.tw, s.status)),
             ("rht_quantize_dy_sr", lambda: nv.nvfp4_rht_quantize(
                 s.dy, 7, nv.ROUND_SR, 7, s.offset, None, s.ady, s.qdy, s.sdy, s.tdy, s.status)),
-            ("rht_quantize_x_rn", lambda: nv.nvfp4_rht_quantize(
-                s.x, 7, nv.ROUND_RN, 0, 0, None, s.axt, s.qxt, s.sxt, s.txt, s.status)),
             ("gemm_fprop", lambda: nv.nvfp4_gemm(
                 s.qx, s.sx, s.tx, nv.BLOCK_1D, s.qw, s.sw, s.tw, nv.BLOCK_2D, s.t, s.f, s.h,
                 s.y)),
@@ -183,12 +187,18 @@ class Step:
         ]
 
     def variant_calls(self):
-        """X's RHT copy with SR (the recipe rounds activations to nearest; the
-        library offers both), timed apart from the step into the step's own
-        X-copy buffers after the step's GEMMs have read them."""
+        """X's two copies as separate calls (the row copy, then the RHT RN
+        copy), and its RHT copy with SR (the recipe rounds activations to
+        nearest; the library offers both), timed apart from the step into the
+        step's own X-copy buffers after the step's GEMMs have read them."""
         nv = self.nv
         s = self
         return [
+            ("quantize_x_1x16", lambda: nv.nvfp4_quantize(
+                s.x, nv.BLOCK_1D, nv.ROUND_RN, 0, 0, nv.OUT_ROW, None, s.ax, s.qx, s.sx, None,
+                None, s.tx, s.status)),
+            ("rht_quantize_x_rn", lambda: nv.nvfp4_rht_quantize(
+                s.x, 7, nv.ROUND_RN, 0, 0, None, s.axt, s.qxt, s.sxt, s.txt, s.status)),
             ("rht_quantize_x_sr", lambda: nv.nvfp4_rht_quantize(
                 s.x, 7, nv.ROUND_SR, 7, s.offset, None, s.axt, s.qxt, s.sxt, s.txt, s.status)),
         ]
@@ -225,6 +235,7 @@ class Step:
         t, h, f = self.t, self.h, self.f
         q1 = 0.5 + 1.0 / 16  # codes + 1x16 scale bytes per element
         return {
+            "quantize_x_row_rht": ("GB/s", t * h * (2 + 2 + 2 * q1)),
             "quantize_x_1x16": ("GB/s", t * h * (2 + 2 + q1)),
             "quantize_w_16x16": ("GB/s", f * h * (2 + 2 + 2 * (0.5 + 1.0 / 256))),
             "rht_quantize_dy_sr": ("GB/s", t * f * (2 + 2 + q1)),
@@ -440,7 +451,9 @@ def main():
         "kernels": kernels,
         "next": ({"dgrad": {k: v for k, v in next_rows.items()
                             if k in ("quantize_dy_1x16_sr", "gemm_dgrad")},
-                  "variants": {k: v for k, v in next_rows.items() if k == "rht_quantize_x_sr"},
+                  "variants": {k: v for k, v in next_rows.items()
+                               if k in ("quantize_x_1x16", "rht_quantize_x_rn",
+                                        "rht_quantize_x_sr")},
                   "mxfp4": {k: v for k, v in next_rows.items() if k.startswith("mx_")},
                   "fp8": {k: v for k, v in next_rows.items() if k.startswith("fp8_")}}
                  if next_rows else None),

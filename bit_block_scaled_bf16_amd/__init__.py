@@ -32,6 +32,7 @@ from ._lib import (  # noqa: F401  (re-exported constants and raw entry points)
     nvfp4_gemm,
     nvfp4_philox_fill,
     nvfp4_quantize,
+    nvfp4_quantize_row_rht,
     nvfp4_rht_quantize,
     nvfp4_rht_sign_mask,
     nvfp4_rht_transform,
@@ -47,6 +48,7 @@ __all__ = [
     "NVFP4Tensor",
     "quantize",
     "rht_quantize",
+    "quantize_row_rht",
     "dequantize",
     "gemm",
     "load",
@@ -135,6 +137,32 @@ def rht_quantize(x, rht_seed: int, rounding: int = ROUND_RN, seed: int = 0, offs
     s = _empty((cols, tokens // 16), torch.uint8, dev)
     nvfp4_rht_quantize(x, rht_seed, rounding, seed, offset, amax, ws, q, s, scale, dev_status)
     return NVFP4Tensor(q, s, scale, BLOCK_1D, cols, tokens), ws
+
+
+def quantize_row_rht(x, rht_seed: int, rounding_t: int = ROUND_RN, seed: int = 0,
+                     offset: int = 0, amax=None, dev_status=None):
+    """Both copies of an activation x [tokens, cols] from one read: the 1x16
+    row copy (round to nearest) and the Hadamard 16x1 column copy, each with
+    its own tensor scale. ``amax`` is None or 2 floats (amax of x, amax of the
+    transformed x).
+
+    Returns (row NVFP4Tensor [tokens, cols], column NVFP4Tensor [cols, tokens],
+    amax workspace or None).
+    """
+    import torch
+
+    tokens, cols = x.shape
+    dev = x.device
+    scale_row, scale_t = _scalar(dev), _scalar(dev)
+    ws = None if amax is not None else amax_workspace(dev)
+    q_row = _empty((tokens, cols // 2), torch.uint8, dev)
+    s_row = _empty((tokens, cols // 16), torch.uint8, dev)
+    q_t = _empty((cols, tokens // 2), torch.uint8, dev)
+    s_t = _empty((cols, tokens // 16), torch.uint8, dev)
+    nvfp4_quantize_row_rht(x, rht_seed, rounding_t, seed, offset, amax, ws, q_row, s_row,
+                           scale_row, q_t, s_t, scale_t, dev_status)
+    return (NVFP4Tensor(q_row, s_row, scale_row, BLOCK_1D, tokens, cols),
+            NVFP4Tensor(q_t, s_t, scale_t, BLOCK_1D, cols, tokens), ws)
 
 
 def dequantize(t: NVFP4Tensor, out_dtype=None):

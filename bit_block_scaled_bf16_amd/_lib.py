@@ -32,6 +32,8 @@ _SIGNATURES = {
                               _P, _P, _P, _P, _P, _P, _P]),
     "nvfp4_rht_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _U64, _INT, _U64, _U32, _P, _P, _P,
                                   _P, _P, _P, _P]),
+    "nvfp4_quantize_row_rht": (_INT, [_P, _INT, _I64, _I64, _I64, _U64, _INT, _U64, _U32, _P,
+                                      _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "nvfp4_dequantize": (_INT, [_P, _P, _P, _I64, _I64, _INT, _INT, _P, _I64, _P]),
     "nvfp4_gemm": (_INT, [_P, _P, _P, _INT, _P, _P, _P, _INT, _I64, _I64, _I64, _P, _INT, _I64,
                           _P]),
@@ -146,6 +148,16 @@ def nvfp4_rht_quantize(x, rht_seed, rounding, seed, offset, amax_in, amax_ws, q_
         _ptr(x), _dtype_code(x), tokens, cols, _ld(x), rht_seed, rounding, seed, offset,
         _ptr(amax_in), _ws(amax_ws), _ptr(q_t), _ptr(s_t), _ptr(tensor_scale),
         _ptr(dev_status), _stream(stream)))
+
+
+def nvfp4_quantize_row_rht(x, rht_seed, rounding_t, seed, offset, amax_in, amax_ws, q_row, s_row,
+                           tensor_scale_row, q_t, s_t, tensor_scale_t, dev_status=None,
+                           stream=None) -> None:
+    tokens, cols = x.shape
+    _check("nvfp4_quantize_row_rht", lib().nvfp4_quantize_row_rht(
+        _ptr(x), _dtype_code(x), tokens, cols, _ld(x), rht_seed, rounding_t, seed, offset,
+        _ptr(amax_in), _ws(amax_ws), _ptr(q_row), _ptr(s_row), _ptr(tensor_scale_row),
+        _ptr(q_t), _ptr(s_t), _ptr(tensor_scale_t), _ptr(dev_status), _stream(stream)))
 
 
 def nvfp4_dequantize(q, s, tensor_scale, rows, cols, block, y, stream=None) -> None:

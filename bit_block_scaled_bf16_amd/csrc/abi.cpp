@@ -143,6 +143,55 @@ int nvfp4_rht_quantize(const void* x, int x_dtype, int64_t tokens, int64_t cols,
   return nvfp4::launch_quantize(q, stream) == 0 ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
+int nvfp4_quantize_row_rht(const void* x, int x_dtype, int64_t tokens, int64_t cols, int64_t ldx,
+                           uint64_t rht_seed, int rounding_t, uint64_t seed, uint32_t offset,
+                           const float* amax_in, float* amax_ws, uint8_t* q_row, uint8_t* s_row,
+                           float* tensor_scale_row, uint8_t* q_t, uint8_t* s_t,
+                           float* tensor_scale_t, int32_t* dev_status, hipStream_t stream) {
+  if (rounding_t != NVFP4_ROUND_RN && rounding_t != NVFP4_ROUND_SR) return NVFP4_ERR_ENUM;
+  int rc = check_input(x, x_dtype, tokens, cols, ldx);
+  if (rc != NVFP4_OK) return rc;
+  if ((tokens % 16) != 0) return NVFP4_ERR_SHAPE;
+  if (tokens > 0 && cols > kMaxElements / tokens) return NVFP4_ERR_SHAPE;
+  if (tensor_scale_row == nullptr || tensor_scale_t == nullptr) return NVFP4_ERR_NULL;
+  if (amax_in == nullptr && amax_ws == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned16(tensor_scale_row) || !aligned16(tensor_scale_t) ||
+      (amax_in && !aligned16(amax_in)) || (amax_ws && !aligned16(amax_ws)) ||
+      (dev_status && !aligned16(dev_status)))
+    return NVFP4_ERR_ALIGN;
+  const bool empty = tokens == 0 || cols == 0;
+  if (!empty) {
+    if (q_row == nullptr || s_row == nullptr || q_t == nullptr || s_t == nullptr)
+      return NVFP4_ERR_NULL;
+    if (!aligned16(q_row) || !aligned16(s_row) || !aligned16(q_t) || !aligned16(s_t))
+      return NVFP4_ERR_ALIGN;
+  }
+  nvfp4::QuantizeLaunch q{};
+  q.x = x;
+  q.x_bf16 = x_dtype == NVFP4_BF16;
+  q.rows = tokens;
+  q.cols = cols;
+  q.ldx = ldx;
+  q.block_2d = false;
+  q.rht = true;
+  q.row_too = true;
+  q.sr = rounding_t == NVFP4_ROUND_SR;
+  q.seed = seed;
+  q.offset = offset;
+  q.sign_mask = nvfp4_rht_sign_mask(rht_seed);
+  q.outputs = NVFP4_OUT_ROW | NVFP4_OUT_COL;
+  q.amax_in = amax_in;
+  q.amax_ws = amax_ws;
+  q.q_row = q_row;
+  q.s_row = s_row;
+  q.q_col = q_t;
+  q.s_col = s_t;
+  q.tensor_scale = tensor_scale_row;
+  q.tensor_scale_t = tensor_scale_t;
+  q.dev_status = dev_status;
+  return nvfp4::launch_quantize(q, stream) == 0 ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
 int nvfp4_dequantize(const uint8_t* q, const uint8_t* s, const float* tensor_scale, int64_t rows,
                      int64_t cols, int block, int out_dtype, void* y, int64_t ldy,
                      hipStream_t stream) {

@@ -18,10 +18,13 @@ struct QuantizeLaunch {
   uint32_t offset;
   uint32_t sign_mask;  // RHT signs (bit i: d_i = -1)
   int outputs;         // 1 = row copy, 2 = column copy (RHT path: column copy)
+  bool row_too;        // RHT path: also the 1x16 row copy (round to nearest) with its
+                       // own tensor scale; amax_in then holds 2 floats (row, Hadamard)
   const float* amax_in;
   float* amax_ws;
   uint8_t *q_row, *s_row, *q_col, *s_col;
-  float* tensor_scale;
+  float* tensor_scale;    // the row copy's (or the only) tensor scale
+  float* tensor_scale_t;  // with row_too: the Hadamard column copy's tensor scale
   int32_t* dev_status;
 };
 

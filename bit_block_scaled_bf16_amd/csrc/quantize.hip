@@ -48,7 +48,9 @@ __device__ __forceinline__ int staged_code_offset(int col, int byte) {
 }
 constexpr int64_t kMaxTileBlocks = 512;  // workgroups of the tile-shaped amax kernel
 
-enum Mode { kMode1D = 0, kMode2D = 1, kModeRHT = 2 };
+// kModeRowRHT: the 1x16 row copy (round to nearest) and the Hadamard column
+// copy of the same tensor, each with its own tensor scale, from one read.
+enum Mode { kMode1D = 0, kMode2D = 1, kModeRHT = 2, kModeRowRHT = 3 };
 
 struct Tile {
   int64_t tr, tc;  // tile coordinates
@@ -160,7 +162,7 @@ __device__ __forceinline__ void rht_columns(float (&v)[16][8], uint32_t sign_mas
 
 // Partials instead of one atomic maximum need no zeroed word before the
 // reduction, so a call is two kernels, not three.
-static_assert(kPartialsOffset + kMaxPartials <= NVFP4_AMAX_WS_BYTES / 4, "workspace size");
+static_assert(kPartialsOffset + 2 * kMaxPartials <= NVFP4_AMAX_WS_BYTES / 4, "workspace size");
 static_assert(kMaxTileBlocks <= kMaxPartials, "one partial per workgroup");
 
 // Block-wide max of per-thread values, written by thread 0 to *dst.
@@ -289,13 +291,20 @@ __device__ __forceinline__ void load_raw_bf16(const uint16_t* __restrict__ x, in
   }
 }
 
-template <typename InT, bool kRht, bool kRagged>
+// With kDual (and kRht) the workgroup also writes the largest magnitude of
+// the untransformed values to partials_plain (the row copy's amax of a
+// tensor quantized both ways in one call).
+template <typename InT, bool kRht, bool kRagged, bool kDual = false>
 __global__ __launch_bounds__(kThreads) void amax_tile_kernel(const InT* __restrict__ x, int64_t rows,
                                                              int64_t cols, int64_t ldx,
                                                              uint32_t sign_mask, int64_t tiles,
-                                                             uint32_t* __restrict__ partials) {
+                                                             uint32_t* __restrict__ partials,
+                                                             uint32_t* __restrict__ partials_plain) {
+  static_assert(!kDual || kRht, "the dual maximum comes with the transform");
   __shared__ uint32_t lds4[kThreads / 64];
+  __shared__ uint32_t lds4_plain[kThreads / 64];
   uint32_t m = 0;
+  uint32_t m_plain = 0;  // bf16: two packed 16-bit maxima; float32: one
   const RhtSigns g = rht_signs(sign_mask);
   if constexpr (sizeof(InT) == 2) {
     // invalid lanes (past the columns) load zeros, which leave the max alone
@@ -308,7 +317,20 @@ __global__ __launch_bounds__(kThreads) void amax_tile_kernel(const InT* __restri
       for (int i = 0; i < 16; ++i) cur[i] = raw[i];
       const int64_t next = tile + gridDim.x;
       if (next < tiles) load_raw_bf16<kRagged>(x, ldx, locate_tile(next, rows, cols), raw);
+      if constexpr (kDual) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          m_plain = max_u16x2(m_plain, cur[i].x & 0x7FFF7FFFu);
+          m_plain = max_u16x2(m_plain, cur[i].y & 0x7FFF7FFFu);
+          m_plain = max_u16x2(m_plain, cur[i].z & 0x7FFF7FFFu);
+          m_plain = max_u16x2(m_plain, cur[i].w & 0x7FFF7FFFu);
+        }
+      }
       m = absmax_bf16_tile<kRht>(cur, g, m);
+    }
+    if constexpr (kDual) {
+      const uint32_t lo = m_plain & 0xFFFFu, hi = m_plain >> 16;
+      m_plain = (lo > hi ? lo : hi) << 16;  // float bits of the larger bf16 magnitude
     }
     // the 1/4 of the transform, applied to the maximum: rounding is
     // monotonic and symmetric, so max |RN(h / 4)| = RN(max |h| / 4)
@@ -319,6 +341,15 @@ __global__ __launch_bounds__(kThreads) void amax_tile_kernel(const InT* __restri
       if (!t.valid) continue;
       float v[16][8];
       load_sub_tile<InT, kRagged>(x, ldx, t.r0, t.c0, t.nrows, v);
+      if constexpr (kDual) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t b = abs_bits(v[i][j]);
+            m_plain = (b > m_plain) ? b : m_plain;
+          }
+      }
       if constexpr (kRht) rht_columns(v, sign_mask);
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -330,6 +361,7 @@ __global__ __launch_bounds__(kThreads) void amax_tile_kernel(const InT* __restri
     }
   }
   block_max_store(m, lds4, partials + blockIdx.x);
+  if constexpr (kDual) block_max_store(m_plain, lds4_plain, partials_plain + blockIdx.x);
 }
 
 // Writes the tensor scale (and the status) for an empty tensor.
@@ -365,6 +397,12 @@ struct QuantParams {
   uint32_t k0, k1, offset;
   uint32_t sign_mask;
   int outputs;
+  // kModeRowRHT: the Hadamard column copy's own amax and tensor scale (the
+  // fields above serve the row copy)
+  const float* amax_in_t;
+  const uint32_t* partials_t;
+  float* amax_out_t;
+  float* tensor_scale_t;
 };
 
 // Scale byte and element multiplier of a block with amax a_b: the byte is
@@ -513,8 +551,11 @@ struct Staging {
 // One workgroup per 256 x 128 tile.
 template <typename InT, int kMode, bool kSR>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
+  constexpr bool kRhtCol = kMode == kModeRHT || kMode == kModeRowRHT;
+  constexpr bool kDualScale = kMode == kModeRowRHT;
   __shared__ __attribute__((aligned(16))) Staging st;
   __shared__ float rtab[128];
+  __shared__ float rtab_t[kDualScale ? 128 : 1];
 
   const int64_t rows = p.rows, cols = p.cols;
   const Tile t = locate(rows, cols);
@@ -525,16 +566,32 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   const float amax = p.amax_in != nullptr ? *p.amax_in : reduce_partials(p.partials, p.n_partials);
   const float s = tensor_scale_from_amax(amax);
   const float six_s = __fmul_rn(6.0f, s);
+  float s_t = s, six_s_t = six_s;
+  if constexpr (kDualScale) {
+    const float amax_t =
+        p.amax_in_t != nullptr ? *p.amax_in_t : reduce_partials(p.partials_t, p.n_partials);
+    s_t = tensor_scale_from_amax(amax_t);
+    six_s_t = __fmul_rn(6.0f, s_t);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      *p.tensor_scale_t = s_t;
+      if (p.amax_out_t != nullptr) *p.amax_out_t = amax_t;
+      if (!(amax_t <= 3.402823466e38f) && p.dev_status != nullptr) *p.dev_status = 1;
+    }
+  }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *p.tensor_scale = s;
     if (p.amax_out != nullptr) *p.amax_out = amax;
     if (!(amax <= 3.402823466e38f) && p.dev_status != nullptr) *p.dev_status = 1;
   }
   fill_recip_table(rtab, s);
+  if constexpr (kDualScale) fill_recip_table(rtab_t, s_t);
   __syncthreads();
+  // the column copy's scale: in kModeRowRHT the Hadamard copy's own
+  const float six_s_col = kDualScale ? six_s_t : six_s;
+  const float* rtab_col = kDualScale ? rtab_t : rtab;
   const RhtSigns g = rht_signs(p.sign_mask);
   const bool out_row = (p.outputs & 1) != 0 && kMode != kModeRHT;
-  const bool out_col = (p.outputs & 2) != 0 || kMode == kModeRHT;
+  const bool out_col = (p.outputs & 2) != 0 || kRhtCol;
   const bool stage_row_scales = out_row && kMode != kMode2D;
   {
     const int c_local0 = t.cg * 8;
@@ -590,7 +647,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) y[j] = __fmul_rn(x8[j], bs.mult);
             uint32_t w;
-            if constexpr (kSR) {
+            if constexpr (kSR && !kDualScale) {
               const uint64_t e = static_cast<uint64_t>(t.r0 + i) * static_cast<uint64_t>(cols) +
                                  static_cast<uint64_t>(t.c0);
               w = pack8_sr(y, sr_words(p.k0, p.k1, e >> 3, p.offset, kStreamRow));
@@ -613,7 +670,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
               c0[i] = cur.get(i, 2 * k);
               c1[i] = cur.get(i, 2 * k + 1);
             }
-            if constexpr (kMode == kModeRHT) {
+            if constexpr (kRhtCol) {
               rht16_unscaled(c0, g);
               rht16_unscaled(c1, g);
             }
@@ -623,8 +680,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
               const uint64_t e0 = static_cast<uint64_t>(t.c0 + j) * static_cast<uint64_t>(rows) +
                                   static_cast<uint64_t>(t.r0);
               uint32_t w0, w1, sb;
-              column_block<kSR, kMode == kModeRHT>(h == 0 ? c0 : c1, six_s, rtab, p.k0, p.k1, e0,
-                                                   p.offset, w0, w1, sb);
+              column_block<kSR, kRhtCol>(h == 0 ? c0 : c1, six_s_col, rtab_col, p.k0, p.k1, e0,
+                                         p.offset, w0, w1, sb);
               uint32_t* dst = reinterpret_cast<uint32_t*>(
                   st.codes + staged_code_offset(c_local0 + j, r_local >> 1));
               dst[0] = w0;
@@ -855,10 +912,13 @@ void launch_quant(const QuantParams& p, hipStream_t stream) {
 
 // Launches the amax kernel for x; returns the number of partial maxima it
 // writes (from ws + kPartialsOffset on), or -1 on a launch error.
+// With dual (rht only) the maxima of the untransformed values follow, from
+// ws + kPartialsOffset + kMaxPartials on.
 template <typename InT>
 int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
-                uint32_t sign_mask, float* amax_ws, hipStream_t stream) {
+                uint32_t sign_mask, float* amax_ws, hipStream_t stream, bool dual = false) {
   uint32_t* partials = reinterpret_cast<uint32_t*>(amax_ws) + kPartialsOffset;
+  uint32_t* partials_plain = partials + kMaxPartials;
   int64_t g;
   if (!rht && ldx == cols) {
     const int64_t n = rows * cols;
@@ -871,15 +931,18 @@ int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
     g = tiles < kMaxTileBlocks ? tiles : kMaxTileBlocks;
     const unsigned gg = static_cast<unsigned>(g);
     const bool ragged = (rows % 16) != 0;
-    if (rht) {
+    if (rht && dual) {
+      amax_tile_kernel<InT, true, false, true><<<gg, kThreads, 0, stream>>>(
+          x, rows, cols, ldx, sign_mask, tiles, partials, partials_plain);
+    } else if (rht) {
       amax_tile_kernel<InT, true, false><<<gg, kThreads, 0, stream>>>(x, rows, cols, ldx, sign_mask,
-                                                                       tiles, partials);
+                                                                       tiles, partials, nullptr);
     } else if (ragged) {
       amax_tile_kernel<InT, false, true><<<gg, kThreads, 0, stream>>>(x, rows, cols, ldx, sign_mask,
-                                                                       tiles, partials);
+                                                                       tiles, partials, nullptr);
     } else {
       amax_tile_kernel<InT, false, false><<<gg, kThreads, 0, stream>>>(x, rows, cols, ldx, sign_mask,
-                                                                        tiles, partials);
+                                                                        tiles, partials, nullptr);
     }
   }
   return hipGetLastError() == hipSuccess ? static_cast<int>(g) : -1;
@@ -894,6 +957,9 @@ void dispatch_quant(const QuantParams& p, int mode, bool sr, hipStream_t stream)
   } else if (mode == kModeRHT) {
     if (sr) launch_quant<InT, kModeRHT, true>(p, stream);
     else launch_quant<InT, kModeRHT, false>(p, stream);
+  } else if (mode == kModeRowRHT) {
+    if (sr) launch_quant<InT, kModeRowRHT, true>(p, stream);
+    else launch_quant<InT, kModeRowRHT, false>(p, stream);
   } else {
     if (sr) launch_quant<InT, kMode1D, true>(p, stream);
     else launch_quant<InT, kMode1D, false>(p, stream);
@@ -933,8 +999,14 @@ __global__ void philox_fill_kernel(uint32_t k0, uint32_t k1, uint32_t c2, uint32
 
 int launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
   const bool bf16 = q.x_bf16;
+  const bool dual = q.rht && q.row_too;
   if (q.rows == 0 || q.cols == 0) {
     empty_tensor_kernel<<<1, 64, 0, stream>>>(q.amax_in, q.amax_ws, q.tensor_scale, q.dev_status);
+    if (dual) {
+      empty_tensor_kernel<<<1, 64, 0, stream>>>(q.amax_in != nullptr ? q.amax_in + 1 : nullptr,
+                                                q.amax_ws != nullptr ? q.amax_ws + 1 : nullptr,
+                                                q.tensor_scale_t, q.dev_status);
+    }
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   QuantParams p;
@@ -942,15 +1014,29 @@ int launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
   p.partials = nullptr;
   p.n_partials = 0;
   p.amax_out = nullptr;
+  p.amax_in_t = dual && q.amax_in != nullptr ? q.amax_in + 1 : nullptr;
+  p.partials_t = nullptr;
+  p.amax_out_t = nullptr;
+  p.tensor_scale_t = q.tensor_scale_t;
   if (q.amax_in == nullptr) {
     const int n = bf16 ? launch_amax(static_cast<const uint16_t*>(q.x), q.rows, q.cols, q.ldx,
-                                     q.rht, q.sign_mask, q.amax_ws, stream)
+                                     q.rht, q.sign_mask, q.amax_ws, stream, dual)
                        : launch_amax(static_cast<const float*>(q.x), q.rows, q.cols, q.ldx,
-                                     q.rht, q.sign_mask, q.amax_ws, stream);
+                                     q.rht, q.sign_mask, q.amax_ws, stream, dual);
     if (n < 0) return -1;
-    p.partials = reinterpret_cast<const uint32_t*>(q.amax_ws) + kPartialsOffset;
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(q.amax_ws) + kPartialsOffset;
     p.n_partials = n;
-    p.amax_out = q.amax_ws;
+    if (dual) {
+      // the row copy: untransformed maxima, amax in ws[0]; the Hadamard copy:
+      // transformed maxima, amax in ws[1]
+      p.partials = base + kMaxPartials;
+      p.amax_out = q.amax_ws;
+      p.partials_t = base;
+      p.amax_out_t = q.amax_ws + 1;
+    } else {
+      p.partials = base;
+      p.amax_out = q.amax_ws;
+    }
   }
   p.x = q.x;
   p.rows = q.rows;
@@ -967,7 +1053,7 @@ int launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
   p.offset = q.offset;
   p.sign_mask = q.sign_mask;
   p.outputs = q.outputs;
-  const int mode = q.rht ? kModeRHT : (q.block_2d ? kMode2D : kMode1D);
+  const int mode = dual ? kModeRowRHT : (q.rht ? kModeRHT : (q.block_2d ? kMode2D : kMode1D));
   if (mode == kMode1D && q.outputs == 1) {
     // the row copy alone streams through its own kernel
     if (bf16) {

@@ -154,6 +154,40 @@ int nvfp4_rht_quantize(const void* x, int x_dtype, int64_t tokens, int64_t cols,
                        float* tensor_scale, int32_t* dev_status, hipStream_t stream);
 
 /*
+ * nvfp4_quantize_row_rht -- both NVFP4 copies of one activation from one
+ * read: the 1x16 row copy (round to nearest, the forward operand) and the
+ * Hadamard-transformed 16x1 column copy of nvfp4_rht_quantize (the
+ * weight-gradient operand). Each copy has its own tensor amax and tensor
+ * scale, so every output equals, bit for bit, that of nvfp4_quantize(block
+ * 1D, RN, OUT_ROW) and of nvfp4_rht_quantize on the same x.
+ * (gist.science summary, Resumen técnico §2 "Formato NVFP4" for the row
+ * copy, "Transformadas de Hadamard Aleatorias (RHT)" for the column copy,
+ * which the recipe applies only to the weight-gradient inputs.)
+ *
+ *   x, x_dtype, tokens, cols, ldx, rht_seed  as nvfp4_rht_quantize.
+ *   rounding_t, seed, offset  rounding of the column copy (and its Philox key
+ *              and counter word 2 for SR); the row copy always rounds to
+ *              nearest.
+ *   amax_in    NULL, or 2 floats: [0] the amax of x, [1] the amax of the
+ *              transformed x.
+ *   amax_ws    NVFP4_AMAX_WS_BYTES of workspace, required when amax_in is
+ *              NULL; afterwards amax_ws[0] and amax_ws[1] hold the two
+ *              amaxes in the order of amax_in.
+ *   q_row, s_row  row copy: codes [tokens][cols/2], scales [tokens][cols/16].
+ *   tensor_scale_row  out: 1 float, the row copy's S.
+ *   q_t, s_t   column copy: codes [cols][tokens/2], scales [cols][tokens/16].
+ *   tensor_scale_t    out: 1 float, the column copy's S.
+ *   dev_status  as nvfp4_quantize (set on either non-finite amax).
+ * tokens == 0 or cols == 0 writes only the two tensor scales (= 1) and
+ * amax_ws[0..1] (= 0). All four output arrays are required otherwise.
+ */
+int nvfp4_quantize_row_rht(const void* x, int x_dtype, int64_t tokens, int64_t cols, int64_t ldx,
+                           uint64_t rht_seed, int rounding_t, uint64_t seed, uint32_t offset,
+                           const float* amax_in, float* amax_ws, uint8_t* q_row, uint8_t* s_row,
+                           float* tensor_scale_row, uint8_t* q_t, uint8_t* s_t,
+                           float* tensor_scale_t, int32_t* dev_status, hipStream_t stream);
+
+/*
  * nvfp4_dequantize -- y = (e2m1(q) * s_f) * S for one stored orientation.
  * (Implied by the format, gist.science summary, Resumen técnico §2 "Formato
  * NVFP4".)
