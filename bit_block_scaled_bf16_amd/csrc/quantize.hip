@@ -496,6 +496,13 @@ struct RawTile<uint16_t> {
     const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
     return (lo > hi ? lo : hi) << 16;
   }
+  // Hides the words from value numbering: a second pass over the tile then
+  // widens them again (one shift or mask per value) instead of keeping the
+  // first pass's 128 widened floats alive, which would halve the occupancy.
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(r[i].x), "+v"(r[i].y), "+v"(r[i].z), "+v"(r[i].w));
+  }
 };
 
 template <>
@@ -516,6 +523,7 @@ struct RawTile<float> {
       }
     return m;
   }
+  __device__ __forceinline__ void opaque() {}
 };
 
 // Loads this lane's 16 x 8 values (lanes past the matrix read zeros). Every
@@ -660,6 +668,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
           }
         }
         if (out_col) {
+          if constexpr (kDualScale) cur.opaque();
           // 16x1 blocks along the rows (tokens), one per column, after the
           // Hadamard transform on the RHT path; two columns at a time
 #pragma unroll

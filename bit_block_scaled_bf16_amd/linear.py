@@ -16,13 +16,19 @@ With X [T, H], W [F, H] and Y = X W^T [T, F]:
                                                           copies, K = tokens)
 Every step runs in the library's kernels (quantizers and GEMMs); the only
 torch work is allocating their outputs. T, H and F must be multiples of 16.
+
+When W needs a gradient, the forward pass quantizes X into both of its
+copies in one call (the 1x16 row copy for fprop, the Hadamard copy for
+wgrad) and keeps only the Hadamard copy for the backward pass: 0.5625 bytes
+per element instead of X's 2.
 """
 
 from __future__ import annotations
 
 import torch
 
-from . import BLOCK_2D, OUT_COL, OUT_ROW, ROUND_RN, ROUND_SR, gemm, quantize, rht_quantize
+from . import (BLOCK_2D, OUT_COL, OUT_ROW, ROUND_RN, ROUND_SR, gemm, quantize, quantize_row_rht,
+               rht_quantize)
 
 
 class NVFP4LinearFunction(torch.autograd.Function):
@@ -32,17 +38,19 @@ class NVFP4LinearFunction(torch.autograd.Function):
     def forward(ctx, x, w, rht_seed: int, sr_seed: int, sr_offset: int):
         if not (x.is_cuda and w.is_cuda):
             raise RuntimeError("NVFP4 linear: tensors must be on the GPU (no CPU path)")
-        qx, _, _ = quantize(x, outputs=OUT_ROW)
+        if ctx.needs_input_grad[1]:
+            qx, qxt, _ = quantize_row_rht(x, rht_seed, rounding_t=ROUND_RN)
+        else:
+            (qx, _, _), qxt = quantize(x, outputs=OUT_ROW), None
         qw, qwt, _ = quantize(w, block=BLOCK_2D, outputs=OUT_ROW | OUT_COL)
         y = gemm(qx, qw)
-        ctx.save_for_backward(x)
+        ctx.qxt = qxt
         ctx.qwt = qwt
         ctx.seeds = (rht_seed, sr_seed, sr_offset)
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        (x,) = ctx.saved_tensors
         rht_seed, sr_seed, sr_offset = ctx.seeds
         dy = dy.contiguous()
         dx = dw = None
@@ -53,8 +61,7 @@ class NVFP4LinearFunction(torch.autograd.Function):
         if ctx.needs_input_grad[1]:
             qdyt, _ = rht_quantize(dy, rht_seed, rounding=ROUND_SR, seed=sr_seed,
                                    offset=sr_offset)
-            qxt, _ = rht_quantize(x, rht_seed, rounding=ROUND_RN)
-            dw = gemm(qdyt, qxt)
+            dw = gemm(qdyt, ctx.qxt)
         return dx, dw, None, None, None
 
 

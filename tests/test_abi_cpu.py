@@ -112,6 +112,34 @@ def test_rht_quantize_argument_errors(L):
     assert r(s_t=MIS) == 4
 
 
+def test_quantize_row_rht_argument_errors(L):
+    def f(**kw):
+        a = dict(x=FAKE, x_dtype=1, tokens=32, cols=32, ldx=32, rht_seed=7, rounding_t=0, seed=0,
+                 offset=0, amax_in=None, amax_ws=FAKE, q_row=FAKE, s_row=FAKE, ts_row=FAKE,
+                 q_t=FAKE, s_t=FAKE, ts_t=FAKE, dev_status=None, stream=None)
+        a.update(kw)
+        return L.nvfp4_quantize_row_rht(*a.values())
+
+    assert f(x_dtype=3) == 3
+    assert f(rounding_t=2) == 3
+    assert f(tokens=24) == 2                        # the Hadamard copy needs tokens % 16
+    assert f(cols=40, ldx=40) == 2
+    assert f(ldx=16) == 2
+    assert f(x=None) == 1
+    assert f(ts_row=None) == 1 and f(ts_t=None) == 1
+    assert f(amax_ws=None) == 1
+    assert f(q_row=None) == 1 and f(s_row=None) == 1
+    assert f(q_t=None) == 1 and f(s_t=None) == 1
+    assert f(x=MIS) == 4
+    assert f(ts_t=MIS) == 4 and f(ts_row=MIS) == 4
+    assert f(amax_in=MIS) == 4
+    assert f(q_row=MIS) == 4 and f(s_t=MIS) == 4
+    # an empty tensor needs no output arrays (only the two tensor scales are
+    # written), so the missing arrays are accepted; nothing is launched here
+    # because the check of the scale pointers comes first and fails
+    assert f(tokens=0, q_row=None, s_row=None, q_t=None, s_t=None, ts_t=None) == 1
+
+
 def test_dequantize_and_gemm_argument_errors(L):
     d = lambda **kw: L.nvfp4_dequantize(*dict(dict(q=FAKE, s=FAKE, ts=FAKE, rows=32, cols=32,
                                                    block=0, out=0, y=FAKE, ldy=32, st=None),

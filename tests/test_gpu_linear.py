@@ -64,6 +64,30 @@ def test_linear_fprop_dgrad_wgrad_match_oracle():
     assert layer.sr_offset == 1
 
 
+def test_linear_frozen_weight_dgrad_only():
+    """With W frozen the forward pass takes the row copy alone (no Hadamard
+    copy); Y and dX match the full layer's, and W gets no gradient."""
+    torch = require_gpu()
+    from bit_block_scaled_bf16_amd.linear import NVFP4Linear
+
+    t, h, f = 128, 64, 96
+    announce(f"linear frozen {t}x{h}->{f}")
+    x_np = wl.normal((t, h), seed=21)
+    dy = to_device(wl.laplace((t, f), seed=22), "bf16")
+    outs = []
+    for frozen in (False, True):
+        layer = NVFP4Linear(h, f, device="cuda")
+        with torch.no_grad():
+            layer.weight.copy_(to_device(wl.weight(f, h, seed=23), "bf16"))
+        layer.weight.requires_grad_(not frozen)
+        x = to_device(x_np, "bf16").requires_grad_(True)
+        y = layer(x)
+        y.backward(dy)
+        outs.append((host(y.float()), host(x.grad.float()), layer.weight.grad))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    assert outs[0][2] is not None and outs[1][2] is None
+
+
 def test_linear_bf16_opt_out():
     torch = require_gpu()
     from bit_block_scaled_bf16_amd.linear import NVFP4Linear
