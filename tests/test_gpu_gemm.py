@@ -56,9 +56,14 @@ def check(c_gpu, ref, absref, k, bf16=True):
 # ragged edges and a ragged K; (4100 | 4312, 4080, *) give 272 tiles, i.e. one
 # full round of 256 x 256 tiles plus a last round of 128 x 128 quarters on
 # 256 CUs, including quarters partly or wholly past the ragged edges.
+# Several rounds of whole 256 x 256 tiles: (4096, 8192, 256) gives 512 tiles,
+# two full rounds; (4352, 8192, 384) two full rounds plus a last round of 32
+# tiles as quarters; (1024, 22784, 256) 356 tiles, a full round and a last
+# round of 100 tiles, too many for quarters.
 @pytest.mark.parametrize("m,n,k", [(16, 16, 16), (256, 256, 64), (300, 520, 80), (512, 768, 1024),
                                    (33, 47, 208), (272, 256, 5120), (2500, 2608, 208),
-                                   (4312, 4080, 336), (4100, 4080, 384)])
+                                   (4312, 4080, 336), (4100, 4080, 384), (4096, 8192, 256),
+                                   (4352, 8192, 384), (1024, 22784, 256)])
 @pytest.mark.parametrize("b_2d", [False, True])
 def test_gemm_parity(m, n, k, b_2d):
     torch = require_gpu()
