@@ -526,21 +526,23 @@ struct RawTile<float> {
   __device__ __forceinline__ void opaque() {}
 };
 
-// Loads this lane's 16 x 8 values (lanes past the matrix read zeros). Every
-// call reaching the tile kernel has rows % 16 == 0, so a lane's 16 rows all
-// exist or none does.
+// Loads this lane's 16 x 8 values. Every call reaching the tile kernel has
+// rows % 16 == 0, so a lane's 16 rows all exist or none does. A lane past the
+// matrix reads the matrix's first 16 x 8 values instead (such calls have at
+// least 16 rows and 16 columns) and never uses them: loads without a
+// condition go out back to back, where a select per load became a branch and
+// a wait per load.
 template <typename InT>
 __device__ __forceinline__ void load_raw(const InT* __restrict__ x, int64_t ldx, const Tile& t,
                                          RawTile<InT>& raw) {
-  const InT* row = x + t.r0 * ldx + t.c0;
+  const InT* row = x + (t.valid ? t.r0 * ldx + t.c0 : 0);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const bool ok = t.valid;
     if constexpr (sizeof(InT) == 2) {
-      raw.r[i] = ok ? *reinterpret_cast<const uint4*>(row) : make_uint4(0u, 0u, 0u, 0u);
+      raw.r[i] = *reinterpret_cast<const uint4*>(row);
     } else {
-      raw.r[i][0] = ok ? *reinterpret_cast<const float4*>(row) : make_float4(0.f, 0.f, 0.f, 0.f);
-      raw.r[i][1] = ok ? *reinterpret_cast<const float4*>(row + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      raw.r[i][0] = *reinterpret_cast<const float4*>(row);
+      raw.r[i][1] = *reinterpret_cast<const float4*>(row + 4);
     }
     row += ldx;
   }
