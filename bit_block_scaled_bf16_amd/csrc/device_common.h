@@ -265,18 +265,27 @@ constexpr int kMaxPartials = 1024;
 // them on its own: 4 loads of 16 bytes per lane, all issued before the
 // first is needed (entries past n hold stale values and are masked off,
 // and the loads stay inside the workspace), then a wave maximum: no LDS, no
-// barrier.
-__device__ __forceinline__ float reduce_partials(const uint32_t* __restrict__ partials, int n) {
+// barrier. The loads and the reduction are separate steps so that a kernel
+// can issue its own loads in between and still wait for these alone
+// (a wave's loads complete in the order they were issued).
+struct PartialWords {
+  uint4 b[kMaxPartials / 256];
+};
+
+__device__ __forceinline__ void load_partials(const uint32_t* __restrict__ partials, PartialWords& w) {
   const int lane = threadIdx.x & 63;
   const uint4* p4 = reinterpret_cast<const uint4*>(partials);
-  uint4 b[kMaxPartials / 256];
 #pragma unroll
-  for (int k = 0; k < kMaxPartials / 256; ++k) b[k] = p4[lane + 64 * k];
+  for (int k = 0; k < kMaxPartials / 256; ++k) w.b[k] = p4[lane + 64 * k];
+}
+
+__device__ __forceinline__ float reduce_loaded_partials(const PartialWords& w, int n) {
+  const int lane = threadIdx.x & 63;
   uint32_t m = 0;
 #pragma unroll
   for (int k = 0; k < kMaxPartials / 256; ++k) {
     const int i = 4 * (lane + 64 * k);
-    const uint32_t v[4] = {b[k].x, b[k].y, b[k].z, b[k].w};
+    const uint32_t v[4] = {w.b[k].x, w.b[k].y, w.b[k].z, w.b[k].w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t x = i + c < n ? v[c] : 0u;
@@ -284,6 +293,12 @@ __device__ __forceinline__ float reduce_partials(const uint32_t* __restrict__ pa
     }
   }
   return __uint_as_float(wave_max_u32(m));
+}
+
+__device__ __forceinline__ float reduce_partials(const uint32_t* __restrict__ partials, int n) {
+  PartialWords w;
+  load_partials(partials, w);
+  return reduce_loaded_partials(w, n);
 }
 
 }  // namespace nvfp4

@@ -569,17 +569,22 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
 
   const int64_t rows = p.rows, cols = p.cols;
   const Tile t = locate(rows, cols);
-  // the tile's loads go out first; the amax (a few more loads) is reduced
-  // while they are in flight
+  // The partial maxima are requested first and the tile right after: the
+  // amax reduction, the reciprocal tables and the barrier then wait only for
+  // the partials, while the tile is still in flight.
+  const bool reduce = p.amax_in == nullptr;
+  const bool reduce_t = kDualScale && p.amax_in_t == nullptr;
+  PartialWords pw{}, pw_t{};
+  if (reduce) load_partials(p.partials, pw);
+  if (reduce_t) load_partials(p.partials_t, pw_t);
   RawTile<InT> cur;
   load_raw<InT>(static_cast<const InT*>(p.x), p.ldx, t, cur);
-  const float amax = p.amax_in != nullptr ? *p.amax_in : reduce_partials(p.partials, p.n_partials);
+  const float amax = reduce ? reduce_loaded_partials(pw, p.n_partials) : *p.amax_in;
   const float s = tensor_scale_from_amax(amax);
   const float six_s = __fmul_rn(6.0f, s);
   float s_t = s, six_s_t = six_s;
   if constexpr (kDualScale) {
-    const float amax_t =
-        p.amax_in_t != nullptr ? *p.amax_in_t : reduce_partials(p.partials_t, p.n_partials);
+    const float amax_t = reduce_t ? reduce_loaded_partials(pw_t, p.n_partials) : *p.amax_in_t;
     s_t = tensor_scale_from_amax(amax_t);
     six_s_t = __fmul_rn(6.0f, s_t);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
