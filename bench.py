@@ -302,6 +302,30 @@ def cpu_baseline():
     }
 
 
+def hbm_copy_reference(torch, reps):
+    """The streaming rate a plain device-to-device copy reaches on this GPU:
+    torch's copy_ between two 1 GiB buffers (ROCm's copy kernel), bytes read
+    plus bytes written per average HIP-event duration. A reference for the
+    quantizers' fractions of the 8 TB/s peak, not a measurement of them."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(max(reps, 1))]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    del src, dst
+    rate = 2 * n / (us * 1e-6) / 1e9
+    return {"GB/s": round(rate, 1), "frac": round(rate / HBM_PEAK_GBS, 4), "us": round(us, 1),
+            "bytes": 2 * n, "what": "torch copy_ of a 1 GiB device buffer (read + write)"}
+
+
 def _cpu_model():
     """The host CPU's model name (from /proc/cpuinfo), or None."""
     try:
@@ -377,6 +401,7 @@ def main():
             next_events[k][i][1].record()
     torch.cuda.synchronize()
     assert int(step.status.cpu()[0]) == 0, "non-finite amax"
+    copy_ref = hbm_copy_reference(torch, args.steps)
 
     ms_step = elapsed * 1e3 / args.steps
     work = step.work()
@@ -458,6 +483,7 @@ def main():
                   "fp8": {k: v for k, v in next_rows.items() if k.startswith("fp8_")}}
                  if next_rows else None),
         "roofline": roofline,
+        "hbm_copy": copy_ref,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
