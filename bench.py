@@ -422,10 +422,12 @@ def main():
                 rate = amount / (avg_ms * 1e-3) / 1e12
                 peak = (FP4_MFMA_PEAK_TFLOPS if unit.startswith("FP4") else
                         FP8_MFMA_PEAK_TFLOPS if unit.startswith("FP8") else MFMA_PEAK_TFLOPS)
+            traffic = profiling.kernel_traffic(summary, CALL_KERNELS[name], CALL_SOURCE[name])
             res[name] = {"us": round(avg_ms * 1e3, 2), "achieved": round(rate, 1), "unit": unit,
-                         "frac": round(rate / peak, 4), "work": amount,
-                         "traffic": profiling.kernel_traffic(summary, CALL_KERNELS[name],
-                                                             CALL_SOURCE[name])}
+                         "frac": round(rate / peak, 4), "work": amount, "traffic": traffic,
+                         # the counted HBM bytes over the same time (null with traffic)
+                         "traffic_GB/s": (round(traffic / (avg_ms * 1e-3) / 1e9, 1)
+                                          if traffic is not None else None)}
         return res
 
     kernels = call_stats(calls, events)
