@@ -326,6 +326,31 @@ def hbm_copy_reference(torch, reps):
             "bytes": 2 * n, "what": "torch copy_ of a 1 GiB device buffer (read + write)"}
 
 
+def dense_gemm_reference(torch, reps, t, h, f):
+    """What ROCm's BLAS reaches on a plain bf16 GEMM of the fprop shape
+    (torch.mm of contiguous random [t, h] and [h, f] operands, fp32
+    accumulation): a reference for the NVFP4 GEMM's fraction of the dense
+    MFMA peak, not a measurement of it."""
+    a = torch.randn(t, h, device="cuda").to(torch.bfloat16)
+    b = torch.randn(h, f, device="cuda").to(torch.bfloat16)
+    out = torch.empty(t, f, device="cuda", dtype=torch.bfloat16)
+    torch.mm(a, b, out=out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(max(reps, 1))]
+    for e0, e1 in ev:
+        e0.record()
+        torch.mm(a, b, out=out)
+        e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+    del a, b, out
+    rate = 2.0 * t * h * f / (us * 1e-6) / 1e12
+    return {"TFLOP/s": round(rate, 1), "frac": round(rate / MFMA_PEAK_TFLOPS, 4),
+            "us": round(us, 1),
+            "what": f"torch.mm bf16 [{t},{h}] x [{h},{f}], random operands (ROCm BLAS)"}
+
+
 def _cpu_model():
     """The host CPU's model name (from /proc/cpuinfo), or None."""
     try:
@@ -402,6 +427,7 @@ def main():
     torch.cuda.synchronize()
     assert int(step.status.cpu()[0]) == 0, "non-finite amax"
     copy_ref = hbm_copy_reference(torch, args.steps)
+    gemm_ref = dense_gemm_reference(torch, args.steps, t, HIDDEN, FFN)
 
     ms_step = elapsed * 1e3 / args.steps
     work = step.work()
@@ -486,6 +512,7 @@ def main():
                  if next_rows else None),
         "roofline": roofline,
         "hbm_copy": copy_ref,
+        "dense_bf16_gemm": gemm_ref,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
