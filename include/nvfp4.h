@@ -21,8 +21,16 @@
  *              r = 1 / (s_f * S), or every code 0 when s_f == 0
  *   per element: y = x * r; q = E2M1 round-to-nearest-even (ties to the code
  *              with mantissa bit 0, |y| > 6 -> 6, sign bit of y kept), or
- *              stochastic: a = min(|y|, 6), round up to the next magnitude
- *              exactly when u16 / 2^16 < (a - lo) / (hi - lo)
+ *              stochastic: a = min(|y|, 6), lo <= a < hi the adjacent E2M1
+ *              magnitudes (lo = hi = 6 when a = 6); round up to hi exactly
+ *              when (a - lo) / (hi - lo) + u16 / 2^16 >= 1, compared exactly
+ *              (the random fraction is added below the step and the sum
+ *              truncated: up-probability floor(frac * 2^16) / 2^16); the
+ *              sign bit of y is kept
+ *   SR example: y = 2.5, u16 = 32767 -> code 0x4; u16 = 32768 -> code 0x5
+ *   SR example: y = -0.75, u16 = 32767 -> code 0x9; u16 = 32768 -> code 0xA
+ *   SR example: y = 0.25, u16 = 32767 -> code 0x0; u16 = 32768 -> code 0x1
+ *   SR example: y = 6.0, u16 = 65535 -> code 0x7
  *   u16 for element e (row-major index of the stored matrix): Philox4x32-10
  *              with key (seed lo, seed hi), counter (e>>3 lo, e>>3 hi,
  *              offset, stream), word (e&7)>>1, half e&1 (0 = low 16 bits);

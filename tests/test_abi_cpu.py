@@ -158,6 +158,10 @@ def test_dequantize_and_gemm_argument_errors(L):
     assert g(ldc=16) == 2
     assert g(ab=1, M=40) == 2
     assert g(bb=1, N=24) == 2
+    # 16x16-blocked operands need their row count to be a multiple of 16
+    assert g(bb=1, M=300, N=520, K=80) == 2
+    assert g(bb=1, M=33, N=47, K=208) == 2
+    assert g(ab=1, M=33, N=48, K=208) == 2
     assert g(ab=3) == 3
     assert g(cd=2) == 3
     assert g(c=None) == 1
@@ -263,3 +267,19 @@ def test_nvfp4_linear_refuses_cpu_tensors_and_opts_out_to_bf16():
         layer(x)
     off = NVFP4Linear(64, 16, nvfp4=False)
     assert torch.equal(off(x), x @ off.weight.t())
+
+
+def test_header_sr_examples_match_the_oracle():
+    """The worked stochastic-rounding examples in include/nvfp4.h state the
+    rule the library implements; the oracle must give the same codes."""
+    text = open(HEADER).read()
+    lines = re.findall(r"SR example: (.*)", text)
+    assert len(lines) >= 3
+    checked = 0
+    for line in lines:
+        y = float(re.match(r"y = ([-+0-9.e]+)", line).group(1))
+        for u16, code in re.findall(r"u16 = (\d+) -> code (0x[0-9A-Fa-f])", line):
+            got = o.e2m1_encode_sr(np.array([y], np.float32), np.array([int(u16)]))[0]
+            assert int(got) == int(code, 16), (y, u16, code, int(got))
+            checked += 1
+    assert checked >= 7

@@ -69,9 +69,18 @@ def test_gemm_parity(m, n, k, b_2d):
     torch = require_gpu()
     import bit_block_scaled_bf16_amd as nv
 
-    if b_2d and n % 16:
-        pytest.skip("2D blocks need N % 16 == 0")
     announce(f"gemm {m}x{n}x{k} b2d={b_2d}")
+    if b_2d and n % 16:
+        # 16x16 blocks need N % 16 == 0: the call is refused before any launch
+        a, _ = quantized_operands(m, 16, k, False, seed=m + n + k)
+        qb = torch.zeros((n, k // 2), dtype=torch.uint8, device="cuda")
+        sb = torch.zeros(((n + 15) // 16, k // 16), dtype=torch.uint8, device="cuda")
+        c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(nv.Nvfp4Error) as err:
+            nv.nvfp4_gemm(a.codes, a.scales, a.tensor_scale, nv.BLOCK_1D, qb, sb, a.tensor_scale,
+                          nv.BLOCK_2D, m, n, k, c)
+        assert err.value.status == nv._lib.ERR_SHAPE
+        return
     a, b = quantized_operands(m, n, k, b_2d, seed=m + n + k)
     ref, absref = reference(a, b)
     c = host(nv.gemm(a, b).float())
