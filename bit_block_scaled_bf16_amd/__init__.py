@@ -32,6 +32,7 @@ from ._lib import (  # noqa: F401  (re-exported constants and raw entry points)
     nvfp4_gemm,
     nvfp4_philox_fill,
     nvfp4_quantize,
+    nvfp4_quantize_noalloc,
     nvfp4_quantize_row_rht,
     nvfp4_rht_quantize,
     nvfp4_rht_sign_mask,

@@ -30,6 +30,8 @@ _INT = ctypes.c_int
 _SIGNATURES = {
     "nvfp4_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _INT, _U64, _U32, _INT, _P, _P,
                               _P, _P, _P, _P, _P, _P, _P]),
+    "nvfp4_quantize_noalloc": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _INT, _U64, _U32, _INT,
+                                      _P, _P, _P, _P, _P, _P, _P, _P]),
     "nvfp4_rht_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _U64, _INT, _U64, _U32, _P, _P, _P,
                                   _P, _P, _P, _P]),
     "nvfp4_quantize_row_rht": (_INT, [_P, _INT, _I64, _I64, _I64, _U64, _INT, _U64, _U32, _P,
@@ -139,6 +141,15 @@ def nvfp4_quantize(x, block, rounding, seed, offset, outputs, amax_in, amax_ws, 
         _ptr(x), _dtype_code(x), rows, cols, _ld(x), block, rounding, seed, offset, outputs,
         _ptr(amax_in), _ws(amax_ws), _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col),
         _ptr(tensor_scale), _ptr(dev_status), _stream(stream)))
+
+
+def nvfp4_quantize_noalloc(x, block, rounding, seed, offset, outputs, amax_in, q_row, s_row,
+                           q_col, s_col, tensor_scale, dev_status=None, stream=None) -> None:
+    rows, cols = x.shape
+    _check("nvfp4_quantize_noalloc", lib().nvfp4_quantize_noalloc(
+        _ptr(x), _dtype_code(x), rows, cols, _ld(x), block, rounding, seed, offset, outputs,
+        _ptr(amax_in), _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _ptr(tensor_scale),
+        _ptr(dev_status), _stream(stream)))
 
 
 def nvfp4_rht_quantize(x, rht_seed, rounding, seed, offset, amax_in, amax_ws, q_t, s_t,

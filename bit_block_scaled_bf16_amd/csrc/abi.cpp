@@ -28,6 +28,59 @@ int check_input(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
 // with 32-bit grid coordinates).
 constexpr int64_t kMaxElements = int64_t(1) << 40;
 
+// The argument checks of nvfp4_quantize; fills q when they pass. With
+// ws_required, amax_ws must be given when amax_in is not (the no-allocation
+// variant brings its own workspace and passes amax_ws = NULL).
+int check_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int block,
+                   int rounding, uint64_t seed, uint32_t offset, int outputs,
+                   const float* amax_in, float* amax_ws, bool ws_required, uint8_t* q_row,
+                   uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, float* tensor_scale,
+                   int32_t* dev_status, nvfp4::QuantizeLaunch& q) {
+  if (block != NVFP4_BLOCK_1D && block != NVFP4_BLOCK_2D) return NVFP4_ERR_ENUM;
+  if (rounding != NVFP4_ROUND_RN && rounding != NVFP4_ROUND_SR) return NVFP4_ERR_ENUM;
+  if (outputs < 1 || outputs > 3) return NVFP4_ERR_ENUM;
+  if (block == NVFP4_BLOCK_2D && rounding == NVFP4_ROUND_SR) return NVFP4_ERR_ENUM;
+  int rc = check_input(x, x_dtype, rows, cols, ldx);
+  if (rc != NVFP4_OK) return rc;
+  const bool out_row = (outputs & NVFP4_OUT_ROW) != 0, out_col = (outputs & NVFP4_OUT_COL) != 0;
+  if ((out_col || block == NVFP4_BLOCK_2D) && (rows % 16) != 0) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && cols > kMaxElements / rows) return NVFP4_ERR_SHAPE;
+  if (tensor_scale == nullptr) return NVFP4_ERR_NULL;
+  if (ws_required && amax_in == nullptr && amax_ws == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned16(tensor_scale) || (amax_in && !aligned16(amax_in)) ||
+      (amax_ws && !aligned16(amax_ws)) || (dev_status && !aligned16(dev_status)))
+    return NVFP4_ERR_ALIGN;
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty) {
+    if (out_row && (q_row == nullptr || s_row == nullptr)) return NVFP4_ERR_NULL;
+    if (out_col && (q_col == nullptr || s_col == nullptr)) return NVFP4_ERR_NULL;
+    if ((out_row && (!aligned16(q_row) || !aligned16(s_row))) ||
+        (out_col && (!aligned16(q_col) || !aligned16(s_col))))
+      return NVFP4_ERR_ALIGN;
+  }
+  q.x = x;
+  q.x_bf16 = x_dtype == NVFP4_BF16;
+  q.rows = rows;
+  q.cols = cols;
+  q.ldx = ldx;
+  q.block_2d = block == NVFP4_BLOCK_2D;
+  q.rht = false;
+  q.sr = rounding == NVFP4_ROUND_SR;
+  q.seed = seed;
+  q.offset = offset;
+  q.sign_mask = 0;
+  q.outputs = outputs;
+  q.amax_in = amax_in;
+  q.amax_ws = amax_ws;
+  q.q_row = q_row;
+  q.s_row = s_row;
+  q.q_col = q_col;
+  q.s_col = s_col;
+  q.tensor_scale = tensor_scale;
+  q.dev_status = dev_status;
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -56,49 +109,31 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
                    int rounding, uint64_t seed, uint32_t offset, int outputs, const float* amax_in,
                    float* amax_ws, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
                    float* tensor_scale, int32_t* dev_status, hipStream_t stream) {
-  if (block != NVFP4_BLOCK_1D && block != NVFP4_BLOCK_2D) return NVFP4_ERR_ENUM;
-  if (rounding != NVFP4_ROUND_RN && rounding != NVFP4_ROUND_SR) return NVFP4_ERR_ENUM;
-  if (outputs < 1 || outputs > 3) return NVFP4_ERR_ENUM;
-  if (block == NVFP4_BLOCK_2D && rounding == NVFP4_ROUND_SR) return NVFP4_ERR_ENUM;
-  int rc = check_input(x, x_dtype, rows, cols, ldx);
-  if (rc != NVFP4_OK) return rc;
-  const bool out_row = (outputs & NVFP4_OUT_ROW) != 0, out_col = (outputs & NVFP4_OUT_COL) != 0;
-  if ((out_col || block == NVFP4_BLOCK_2D) && (rows % 16) != 0) return NVFP4_ERR_SHAPE;
-  if (rows > 0 && cols > kMaxElements / rows) return NVFP4_ERR_SHAPE;
-  if (tensor_scale == nullptr) return NVFP4_ERR_NULL;
-  if (amax_in == nullptr && amax_ws == nullptr) return NVFP4_ERR_NULL;
-  if (!aligned16(tensor_scale) || (amax_in && !aligned16(amax_in)) ||
-      (amax_ws && !aligned16(amax_ws)) || (dev_status && !aligned16(dev_status)))
-    return NVFP4_ERR_ALIGN;
-  const bool empty = rows == 0 || cols == 0;
-  if (!empty) {
-    if (out_row && (q_row == nullptr || s_row == nullptr)) return NVFP4_ERR_NULL;
-    if (out_col && (q_col == nullptr || s_col == nullptr)) return NVFP4_ERR_NULL;
-    if ((out_row && (!aligned16(q_row) || !aligned16(s_row))) ||
-        (out_col && (!aligned16(q_col) || !aligned16(s_col))))
-      return NVFP4_ERR_ALIGN;
-  }
   nvfp4::QuantizeLaunch q{};
-  q.x = x;
-  q.x_bf16 = x_dtype == NVFP4_BF16;
-  q.rows = rows;
-  q.cols = cols;
-  q.ldx = ldx;
-  q.block_2d = block == NVFP4_BLOCK_2D;
-  q.rht = false;
-  q.sr = rounding == NVFP4_ROUND_SR;
-  q.seed = seed;
-  q.offset = offset;
-  q.sign_mask = 0;
-  q.outputs = outputs;
-  q.amax_in = amax_in;
-  q.amax_ws = amax_ws;
-  q.q_row = q_row;
-  q.s_row = s_row;
-  q.q_col = q_col;
-  q.s_col = s_col;
-  q.tensor_scale = tensor_scale;
-  q.dev_status = dev_status;
+  int rc = check_quantize(x, x_dtype, rows, cols, ldx, block, rounding, seed, offset, outputs,
+                          amax_in, amax_ws, true, q_row, s_row, q_col, s_col, tensor_scale,
+                          dev_status, q);
+  if (rc != NVFP4_OK) return rc;
+  return nvfp4::launch_quantize(q, stream) == 0 ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+int nvfp4_quantize_noalloc(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                           int block, int rounding, uint64_t seed, uint32_t offset, int outputs,
+                           const float* amax_in, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                           uint8_t* s_col, float* tensor_scale, int32_t* dev_status,
+                           hipStream_t stream) {
+  nvfp4::QuantizeLaunch q{};
+  int rc = check_quantize(x, x_dtype, rows, cols, ldx, block, rounding, seed, offset, outputs,
+                          amax_in, nullptr, false, q_row, s_row, q_col, s_col, tensor_scale,
+                          dev_status, q);
+  if (rc != NVFP4_OK) return rc;
+  if (amax_in == nullptr) {
+    int64_t floats = 0;
+    float* ws = nvfp4::static_amax_workspace(&floats);
+    if (ws == nullptr) return NVFP4_ERR_HIP;
+    q.amax_ws = ws;
+    if (nvfp4::quantize_workspace_floats(q) > floats) return NVFP4_ERR_SHAPE;
+  }
   return nvfp4::launch_quantize(q, stream) == 0 ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

@@ -31,6 +31,14 @@ struct QuantizeLaunch {
 // Each returns 0, or -1 when a launch failed.
 int launch_quantize(const QuantizeLaunch& q, hipStream_t stream);
 
+// Floats of amax_ws (from its start) that launch_quantize(q) writes or reads.
+int64_t quantize_workspace_floats(const QuantizeLaunch& q);
+
+// The library's own amax workspace on the current device (a static device
+// array; see noalloc.hip), or NULL when its address cannot be found.
+// *floats receives its size in floats.
+float* static_amax_workspace(int64_t* floats);
+
 int launch_dequantize(const uint8_t* q, const uint8_t* s, const float* tensor_scale, int64_t rows,
                       int64_t cols, bool block_2d, bool out_bf16, void* y, int64_t ldy,
                       hipStream_t stream);

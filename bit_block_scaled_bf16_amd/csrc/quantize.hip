@@ -930,21 +930,30 @@ void launch_quant(const QuantParams& p, hipStream_t stream) {
 // writes (from ws + kPartialsOffset on), or -1 on a launch error.
 // With dual (rht only) the maxima of the untransformed values follow, from
 // ws + kPartialsOffset + kMaxPartials on.
+// Workgroups of the amax kernel launch_amax picks for x, i.e. the number of
+// partial maxima it writes (per set of maxima).
+int64_t amax_workgroups(int64_t rows, int64_t cols, int64_t ldx, bool rht, int64_t elem_bytes) {
+  if (!rht && ldx == cols) {
+    const int64_t n = rows * cols;
+    const int64_t per_block = static_cast<int64_t>(kThreads) * kFlatUnroll * (16 / elem_bytes);
+    const int64_t g = (n + per_block - 1) / per_block;
+    return g > kMaxPartials ? kMaxPartials : g;
+  }
+  const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
+  return tiles < kMaxTileBlocks ? tiles : kMaxTileBlocks;
+}
+
 template <typename InT>
 int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
                 uint32_t sign_mask, float* amax_ws, hipStream_t stream, bool dual = false) {
   uint32_t* partials = reinterpret_cast<uint32_t*>(amax_ws) + kPartialsOffset;
   uint32_t* partials_plain = partials + kMaxPartials;
-  int64_t g;
+  const int64_t g = amax_workgroups(rows, cols, ldx, rht, sizeof(InT));
   if (!rht && ldx == cols) {
-    const int64_t n = rows * cols;
-    const int64_t per_block = static_cast<int64_t>(kThreads) * kFlatUnroll * (16 / sizeof(InT));
-    g = (n + per_block - 1) / per_block;
-    if (g > kMaxPartials) g = kMaxPartials;
-    amax_flat_kernel<InT><<<static_cast<unsigned>(g), kThreads, 0, stream>>>(x, n, partials);
+    amax_flat_kernel<InT><<<static_cast<unsigned>(g), kThreads, 0, stream>>>(x, rows * cols,
+                                                                             partials);
   } else {
     const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
-    g = tiles < kMaxTileBlocks ? tiles : kMaxTileBlocks;
     const unsigned gg = static_cast<unsigned>(g);
     const bool ragged = (rows % 16) != 0;
     if (rht && dual) {
@@ -1012,6 +1021,14 @@ __global__ void philox_fill_kernel(uint32_t k0, uint32_t k1, uint32_t c2, uint32
 }
 
 }  // namespace
+
+int64_t quantize_workspace_floats(const QuantizeLaunch& q) {
+  if (q.rows == 0 || q.cols == 0) return q.amax_in == nullptr ? (q.rht && q.row_too ? 2 : 1) : 0;
+  if (q.amax_in != nullptr) return 0;
+  const int64_t g = amax_workgroups(q.rows, q.cols, q.ldx, q.rht, q.x_bf16 ? 2 : 4);
+  // the second set of maxima (the untransformed ones) starts kMaxPartials later
+  return kPartialsOffset + ((q.rht && q.row_too) ? kMaxPartials : 0) + g;
+}
 
 int launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
   const bool bf16 = q.x_bf16;

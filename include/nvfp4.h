@@ -137,6 +137,33 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
                    hipStream_t stream);
 
 /*
+ * nvfp4_quantize_noalloc -- nvfp4_quantize for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, hosts that
+ * forbid allocation): the same arguments without amax_ws, the same outputs
+ * bit for bit. The amax pass uses a workspace inside the library instead: a
+ * static device array of NVFP4_AMAX_WS_BYTES (16 KiB) per GPU, held until
+ * the process ends. Its device address is looked up on the first call on
+ * each device (with that device current); no call allocates or frees
+ * memory, or synchronises.
+ *
+ *   Every call on one GPU shares that GPU's workspace, and each call leaves
+ *   its partial maxima in it (none needs an initial value). Calls whose work
+ *   may overlap on one GPU (different streams, unordered host threads) race
+ *   on it: order them on one stream. The workspace need does not grow with
+ *   the tensor (at most NVFP4_AMAX_WS_BYTES for any shape nvfp4_quantize
+ *   accepts); a call that would need more returns NVFP4_ERR_SHAPE. The
+ *   tensor amax itself is not returned (tensor_scale is).
+ *   Errors: those of nvfp4_quantize (amax_in == NULL is allowed), checked
+ *   before any HIP call; NVFP4_ERR_HIP when the workspace's address cannot
+ *   be found or a launch fails.
+ */
+int nvfp4_quantize_noalloc(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                           int block, int rounding, uint64_t seed, uint32_t offset, int outputs,
+                           const float* amax_in, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                           uint8_t* s_col, float* tensor_scale, int32_t* dev_status,
+                           hipStream_t stream);
+
+/*
  * nvfp4_rht_quantize -- weight-gradient operand path: 16-point random
  * Hadamard transform along the token dimension, then 16x1 NVFP4 blocks along
  * tokens, stored transposed so the token dimension is the GEMM K dimension.

@@ -96,6 +96,32 @@ def test_quantize_argument_errors(L):
     assert q(L, x_dtype=0, ldx=34) == 4             # fp32 rows of 136 bytes
 
 
+def test_quantize_noalloc_argument_errors(L):
+    """The no-allocation variant checks its arguments like nvfp4_quantize,
+    before any HIP call (it has no amax_ws; amax_in may be NULL)."""
+    def n(**kw):
+        a = dict(x=FAKE, x_dtype=1, rows=32, cols=32, ldx=32, block=0, rounding=0, seed=0,
+                 offset=0, outputs=3, amax_in=FAKE, q_row=FAKE, s_row=FAKE, q_col=FAKE,
+                 s_col=FAKE, tensor_scale=FAKE, dev_status=None, stream=None)
+        a.update(kw)
+        return L.nvfp4_quantize_noalloc(*a.values())
+
+    assert n(x_dtype=7) == 3
+    assert n(block=2) == 3
+    assert n(block=1, rounding=1) == 3
+    assert n(outputs=0) == 3
+    assert n(cols=24, ldx=24) == 2
+    assert n(rows=24) == 2
+    assert n(ldx=16) == 2
+    assert n(x=None) == 1
+    assert n(tensor_scale=None) == 1
+    assert n(amax_in=None, tensor_scale=None) == 1
+    assert n(q_col=None) == 1
+    assert n(x=MIS) == 4
+    assert n(amax_in=MIS) == 4
+    assert n(q_row=MIS) == 4
+
+
 def test_rht_quantize_argument_errors(L):
     def r(**kw):
         a = dict(x=FAKE, x_dtype=1, tokens=32, cols=32, ldx=32, rht_seed=7, rounding=1, seed=7,
