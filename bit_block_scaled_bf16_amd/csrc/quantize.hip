@@ -46,7 +46,7 @@ constexpr int kLdsCodeStride = kTileRows / 2;  // bytes per staged column
 __device__ __forceinline__ int staged_code_offset(int col, int byte) {
   return col * kLdsCodeStride + ((((byte >> 4) ^ ((col >> 3) & 7)) << 4) | (byte & 15));
 }
-constexpr int64_t kMaxTileBlocks = 512;  // workgroups of the tile-shaped amax kernel
+constexpr int64_t kMaxTileBlocks = 1024;  // workgroups of the tile-shaped amax kernels
 
 // kModeRowRHT: the 1x16 row copy (round to nearest) and the Hadamard column
 // copy of the same tensor, each with its own tensor scale, from one read.
@@ -405,6 +405,31 @@ struct QuantParams {
   float* tensor_scale_t;
 };
 
+// Random words of stochastic rounding for one launch and one copy (stream):
+// the launch-constant form of Philox when every counter's g fits 32 bits
+// (fewer than 2^35 elements; a uniform branch), the plain one otherwise.
+struct SrKey {
+  PhiloxSr ps;
+  uint32_t k0, k1, offset, stream;
+  bool small;
+};
+
+__device__ __forceinline__ SrKey sr_key(const QuantParams& p, uint32_t stream) {
+  SrKey k;
+  k.ps = philox_sr_setup(p.k0, p.k1, p.offset, stream);
+  k.k0 = p.k0;
+  k.k1 = p.k1;
+  k.offset = p.offset;
+  k.stream = stream;
+  k.small = static_cast<uint64_t>(p.rows) * static_cast<uint64_t>(p.cols) < (uint64_t(1) << 35);
+  return k;
+}
+
+__device__ __forceinline__ U4 words_for(const SrKey& k, uint64_t g) {
+  if (k.small) return sr_words_fast(k.ps, static_cast<uint32_t>(g));
+  return sr_words(k.k0, k.k1, g, k.offset, k.stream);
+}
+
 // Scale byte and element multiplier of a block with amax a_b: the byte is
 // E4M3(fp32(a_b / 6S)); the multiplier r = fp32(1 / fp32(s_f S)) comes from
 // the workgroup's table of the 127 byte values (0 for the zero byte).
@@ -413,9 +438,42 @@ struct BlockMult {
   float mult;
 };
 
-__device__ __forceinline__ BlockMult block_mult(float amax_b, float six_s, const float* rtab) {
+// Division by the tensor's 6 S, which every block of a launch shares. With
+// y = fp32(1 / d) taken once, q0 = fp32(a y), the remainder r = a - q0 d
+// (exact in one fused multiply-add) and fp32(q0 + r y) (one more) give the
+// correctly rounded quotient fp32(a / d) (Markstein's correction step; a
+// CPU check found no exception in 3e10 cases with d in [2^-60, 2^120] and
+// quotients in [2^-12, 2^13], and quotients outside that range are either
+// far below E4M3's smallest step or saturate). The remainder must not be a
+// float32 subnormal, so for d < 2^-60 (a tensor amax below about 2^-52) the
+// division is a plain IEEE division instead: the branch is uniform.
+struct ScaleDiv {
+  float d, y;
+  bool fast;
+};
+
+__device__ __forceinline__ ScaleDiv scale_div(float six_s) {
+  ScaleDiv sd;
+  // the same value in every lane; made explicit so that the branch in div_by
+  // is a scalar one
+  sd.d = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(six_s)));
+  sd.y = __fdiv_rn(1.0f, sd.d);
+  sd.fast = sd.d >= 0x1p-60f;
+  return sd;
+}
+
+__device__ __forceinline__ float div_by(float a, const ScaleDiv& sd) {
+  if (sd.fast) {
+    const float q0 = __fmul_rn(a, sd.y);
+    const float r = __builtin_fmaf(-q0, sd.d, a);
+    return __builtin_fmaf(r, sd.y, q0);
+  }
+  return __fdiv_rn(a, sd.d);
+}
+
+__device__ __forceinline__ BlockMult block_mult(float amax_b, const ScaleDiv& six_s, const float* rtab) {
   BlockMult b;
-  b.byte = e4m3_from_float(__fdiv_rn(amax_b, six_s));
+  b.byte = e4m3_from_float(div_by(amax_b, six_s));
   b.mult = rtab[b.byte];
   return b;
 }
@@ -443,10 +501,9 @@ __device__ __forceinline__ float abs_max(const float* v) {
 // are those of quantizing the scaled values, unless a scaled value or r / 4
 // would be a float32 subnormal.
 template <bool kSR, bool kQuarter>
-__device__ __forceinline__ void column_block(const float (&col)[16], float six_s, const float* rtab,
-                                             uint32_t k0, uint32_t k1, uint64_t e0,
-                                             uint32_t offset, uint32_t& w0, uint32_t& w1,
-                                             uint32_t& sbyte) {
+__device__ __forceinline__ void column_block(const float (&col)[16], const ScaleDiv& six_s, const float* rtab,
+                                             const SrKey& key, uint64_t e0, uint32_t& w0,
+                                             uint32_t& w1, uint32_t& sbyte) {
   float am = abs_max<16>(col);
   if constexpr (kQuarter) am = __fmul_rn(am, 0.25f);
   BlockMult bm = block_mult(am, six_s, rtab);
@@ -456,8 +513,8 @@ __device__ __forceinline__ void column_block(const float (&col)[16], float six_s
   for (int i = 0; i < 16; ++i) y[i] = __fmul_rn(col[i], bm.mult);
   if constexpr (kSR) {
     const uint64_t g = e0 >> 3;
-    w0 = pack8_sr(y, sr_words(k0, k1, g, offset, kStreamCol));
-    w1 = pack8_sr(y + 8, sr_words(k0, k1, g + 1, offset, kStreamCol));
+    w0 = pack8_sr(y, words_for(key, g));
+    w1 = pack8_sr(y + 8, words_for(key, g + 1));
   } else {
     w0 = pack8_rn(y);
     w1 = pack8_rn(y + 8);
@@ -526,7 +583,8 @@ struct RawTile<float> {
   __device__ __forceinline__ void opaque() {}
 };
 
-// Loads this lane's 16 x 8 values. Every call reaching the tile kernel has
+// Loads this lane's 16 x 8 values (nontemporal: the tile is read once). Every
+// call reaching the tile kernel has
 // rows % 16 == 0, so a lane's 16 rows all exist or none does. A lane past the
 // matrix reads the matrix's first 16 x 8 values instead (such calls have at
 // least 16 rows and 16 columns) and never uses them: loads without a
@@ -539,10 +597,13 @@ __device__ __forceinline__ void load_raw(const InT* __restrict__ x, int64_t ldx,
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     if constexpr (sizeof(InT) == 2) {
-      raw.r[i] = *reinterpret_cast<const uint4*>(row);
+      raw.r[i] = load_stream(row);
     } else {
-      raw.r[i][0] = *reinterpret_cast<const float4*>(row);
-      raw.r[i][1] = *reinterpret_cast<const float4*>(row + 4);
+      const uint4 a = load_stream(row), b = load_stream(row + 4);
+      raw.r[i][0] = make_float4(__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
+                                __uint_as_float(a.w));
+      raw.r[i][1] = make_float4(__uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z),
+                                __uint_as_float(b.w));
     }
     row += ldx;
   }
@@ -557,6 +618,72 @@ struct Staging {
   uint8_t col_scales[kTileCols * 16];
   uint8_t row_scales[kTileRows * 8];
 };
+
+// Writes a tile's staged outputs after the barrier that ends its staging:
+// the row-block scales (8 bytes per row of the tile) and the column copy
+// (128 code bytes and, with col_scales, 16 scale bytes per column).
+__device__ __forceinline__ void store_staged(const Staging& st, const QuantParams& p, int64_t tr,
+                                             int64_t tc, bool stage_row_scales, bool out_col,
+                                             bool col_scales) {
+  const int64_t rows = p.rows, cols = p.cols;
+  const int tid = threadIdx.x;
+  if (stage_row_scales) {
+    // one row's 8 scale bytes of this tile per thread
+    const int64_t row = tr * kTileRows + tid;
+    const int64_t nblk = (cols - tc * kTileCols) < kTileCols ? (cols - tc * kTileCols) >> 4 : 8;
+    if (row < rows) {
+      uint8_t* dst = p.s_row + row * (cols >> 4) + tc * 8;
+      if (nblk == 8 && ((cols >> 4) & 7) == 0) {
+        *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(st.row_scales + tid * 8);
+      } else {
+        for (int b = 0; b < nblk; ++b) dst[b] = st.row_scales[tid * 8 + b];
+      }
+    }
+  }
+  if (out_col) {
+    // each column's codes for this tile's rows are contiguous in q_col: 8
+    // lanes write one column's 128 bytes as 16-byte granules (8-byte chunks
+    // when rows % 32 != 0 leaves column starts only 8-byte aligned), and its
+    // 16 scale bytes (1D) leave as one store where alignment allows
+    const int64_t rows_here = (rows - tr * kTileRows) < kTileRows ? (rows - tr * kTileRows) : kTileRows;
+    const int code_chunks = static_cast<int>(rows_here >> 4);  // 8-byte chunks per column
+    if ((rows & 31) == 0) {
+      const int granules = code_chunks >> 1;
+#pragma unroll
+      for (int k = tid; k < kTileCols * (kTileRows / 32); k += kThreads) {
+        const int c_local = k >> 3, g = k & 7;
+        const int64_t col = tc * kTileCols + c_local;
+        if (col < cols && g < granules) {
+          const uint4 val = *reinterpret_cast<const uint4*>(st.codes + staged_code_offset(c_local, 16 * g));
+          *reinterpret_cast<uint4*>(p.q_col + col * (rows >> 1) + tr * (kTileRows / 2) + 16 * g) = val;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = tid; k < kTileCols * (kTileRows / 16); k += kThreads) {
+        const int c_local = k >> 4, ch = k & 15;
+        const int64_t col = tc * kTileCols + c_local;
+        if (col < cols && ch < code_chunks) {
+          const uint2 val = *reinterpret_cast<const uint2*>(st.codes + staged_code_offset(c_local, 8 * ch));
+          *reinterpret_cast<uint2*>(p.q_col + col * (rows >> 1) + tr * (kTileRows / 2) + ch * 8) = val;
+        }
+      }
+    }
+    if (col_scales) {
+      if (tid < kTileCols) {
+        const int64_t col = tc * kTileCols + tid;
+        if (col < cols) {
+          uint8_t* dst = p.s_col + col * (rows >> 4) + tr * (kTileRows / 16);
+          if (code_chunks == 16 && ((rows >> 4) & 15) == 0) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(st.col_scales + tid * 16);
+          } else {
+            for (int b = 0; b < code_chunks; ++b) dst[b] = st.col_scales[tid * 16 + b];
+          }
+        }
+      }
+    }
+  }
+}
 
 // One workgroup per 256 x 128 tile.
 template <typename InT, int kMode, bool kSR>
@@ -581,12 +708,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   load_raw<InT>(static_cast<const InT*>(p.x), p.ldx, t, cur);
   const float amax = reduce ? reduce_loaded_partials(pw, p.n_partials) : *p.amax_in;
   const float s = tensor_scale_from_amax(amax);
-  const float six_s = __fmul_rn(6.0f, s);
-  float s_t = s, six_s_t = six_s;
+  const ScaleDiv six_s = scale_div(__fmul_rn(6.0f, s));
+  float s_t = s;
+  ScaleDiv six_s_t = six_s;
   if constexpr (kDualScale) {
     const float amax_t = reduce_t ? reduce_loaded_partials(pw_t, p.n_partials) : *p.amax_in_t;
     s_t = tensor_scale_from_amax(amax_t);
-    six_s_t = __fmul_rn(6.0f, s_t);
+    six_s_t = scale_div(__fmul_rn(6.0f, s_t));
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       *p.tensor_scale_t = s_t;
       if (p.amax_out_t != nullptr) *p.amax_out_t = amax_t;
@@ -602,9 +730,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   if constexpr (kDualScale) fill_recip_table(rtab_t, s_t);
   __syncthreads();
   // the column copy's scale: in kModeRowRHT the Hadamard copy's own
-  const float six_s_col = kDualScale ? six_s_t : six_s;
+  const ScaleDiv six_s_col = kDualScale ? six_s_t : six_s;
   const float* rtab_col = kDualScale ? rtab_t : rtab;
   const RhtSigns g = rht_signs(p.sign_mask);
+  const SrKey key_row = sr_key(p, kStreamRow), key_col = sr_key(p, kStreamCol);
   const bool out_row = (p.outputs & 1) != 0 && kMode != kModeRHT;
   const bool out_col = (p.outputs & 2) != 0 || kRhtCol;
   const bool stage_row_scales = out_row && kMode != kMode2D;
@@ -665,7 +794,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
             if constexpr (kSR && !kDualScale) {
               const uint64_t e = static_cast<uint64_t>(t.r0 + i) * static_cast<uint64_t>(cols) +
                                  static_cast<uint64_t>(t.c0);
-              w = pack8_sr(y, sr_words(p.k0, p.k1, e >> 3, p.offset, kStreamRow));
+              w = pack8_sr(y, words_for(key_row, e >> 3));
             } else {
               w = pack8_rn(y);
             }
@@ -696,8 +825,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
               const uint64_t e0 = static_cast<uint64_t>(t.c0 + j) * static_cast<uint64_t>(rows) +
                                   static_cast<uint64_t>(t.r0);
               uint32_t w0, w1, sb;
-              column_block<kSR, kRhtCol>(h == 0 ? c0 : c1, six_s_col, rtab_col, p.k0, p.k1, e0,
-                                         p.offset, w0, w1, sb);
+              column_block<kSR, kRhtCol>(h == 0 ? c0 : c1, six_s_col, rtab_col, key_col, e0, w0, w1,
+                                         sb);
               uint32_t* dst = reinterpret_cast<uint32_t*>(
                   st.codes + staged_code_offset(c_local0 + j, r_local >> 1));
               dst[0] = w0;
@@ -711,62 +840,472 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
 
     if (!out_col && !stage_row_scales) return;
     __syncthreads();
-    const int tid = threadIdx.x;
-    const int64_t tr = t.tr, tc = t.tc;
-    if (stage_row_scales) {
-      // one row's 8 scale bytes of this tile per thread
-      const int64_t row = tr * kTileRows + tid;
-      const int64_t nblk = (cols - tc * kTileCols) < kTileCols ? (cols - tc * kTileCols) >> 4 : 8;
-      if (row < rows) {
-        uint8_t* dst = p.s_row + row * (cols >> 4) + tc * 8;
-        if (nblk == 8 && ((cols >> 4) & 7) == 0) {
-          *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(st.row_scales + tid * 8);
-        } else {
-          for (int b = 0; b < nblk; ++b) dst[b] = st.row_scales[tid * 8 + b];
+    store_staged(st, p, t.tr, t.tc, stage_row_scales, out_col, kMode != kMode2D);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The Hadamard path of bf16 inputs on the matrix cores.
+//
+// A 16-token block of one column transforms as x' = A x with
+// A = H diag(d) / 4, whose entries are +-1/4 and exact in bf16. So
+// v_mfma_f32_16x16x16_bf16 forms every product exactly and sums them in
+// float32. Its results are within one float32 unit of the block's largest
+// magnitude of the exact transform (measured on MI355X), and the same inputs
+// always give the same bits, so the amax pass, the quantize pass and the
+// inspection hook agree exactly. (float32 inputs keep the butterfly.)
+//
+// Lane layout of the MFMA operands: lane l owns the 4 consecutive tokens
+// 4 (l / 16) + i (i = 0..3) of a 16-token step and the 8 consecutive columns
+// 8 (l % 16) + j (j = 0..7), i.e. four 16-byte loads. MFMA j takes the lane's
+// column j (4 tokens) as its B operand and the lane's slice of A, and
+// returns the transformed values of the same 4 tokens of column j: each lane
+// ends up holding its own 4 x 8 block, transformed. A 16x1 column block then
+// lies in the 4 lanes with the same l % 16; a 1x16 row block (the row copy)
+// in lanes 2m and 2m + 1. The workgroup keeps the 256 x 128 tile of the
+// other modes; wave w owns its tokens 64 w .. 64 w + 63 as 4 steps of 16.
+// ---------------------------------------------------------------------------
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kSteps = 4;  // 16-token steps per wave and tile
+static_assert(kTileRows == (kThreads / 64) * 16 * kSteps, "each wave owns 4 steps of the tile");
+
+// Lane l's A operand: A[m][k] for m = l % 16, k = 4 (l / 16) + v, i.e.
+// (-1)^popcount(m & k) * d_k / 4 as bf16 (+-0.25 = 0x3E80 / 0xBE80).
+__device__ __forceinline__ bf16x4_t rht_a_operand(uint32_t sign_mask) {
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 15, k0 = 4 * (lane >> 4);
+  bf16x4_t a;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int k = k0 + v;
+    const uint32_t neg = (static_cast<uint32_t>(__popc(m & k)) ^ (sign_mask >> k)) & 1u;
+    a[v] = static_cast<short>(neg ? 0xBE80 : 0x3E80);
+  }
+  return a;
+}
+
+template <int q>
+__device__ __forceinline__ uint32_t word_of(const uint4& r) {
+  return q == 0 ? r.x : q == 1 ? r.y : q == 2 ? r.z : r.w;
+}
+
+// Transformed values of the lane's column j from its 4 token rows (8 bf16
+// each): the j-th bf16 of every row, paired into the B operand by two byte
+// permutes, then one MFMA. Result v = token 4 (l / 16) + v of column j.
+template <int j>
+__device__ __forceinline__ f32x4_t rht_mfma(bf16x4_t a, const uint4* rows4) {
+  constexpr uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+  const uint32_t lo = __builtin_amdgcn_perm(word_of<j / 2>(rows4[1]), word_of<j / 2>(rows4[0]), sel);
+  const uint32_t hi = __builtin_amdgcn_perm(word_of<j / 2>(rows4[3]), word_of<j / 2>(rows4[2]), sel);
+  const u32x2_t b = {lo, hi};
+  const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(bf16x4_t, b), zero, 0, 0, 0);
+}
+
+// maximum(m, |a|, |b|), propagating NaN (a NaN or an infinity in the data
+// must reach the tensor amax and the status flag).
+__device__ __forceinline__ float max3_abs(float m, float a, float b) {
+  float r;
+  asm("v_maximum3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
+__device__ __forceinline__ float max_of(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Largest magnitude of one column's 4 transformed values of this lane.
+__device__ __forceinline__ float col_absmax(const f32x4_t& o) {
+  return max3_abs(max3_abs(0.0f, o[0], o[1]), o[2], o[3]);
+}
+
+struct MfmaTile {
+  int64_t tr, tc;
+  int64_t r0;      // token of this lane's first row in step 0
+  int64_t c0;      // first of this lane's 8 columns
+  int steps;       // this wave's steps inside the matrix (0..4), wave-uniform
+  bool col_valid;  // the lane's columns exist
+};
+
+// kColMajor numbers the tiles down the token dimension first. A column copy
+// alone then has the workgroups that run together on an XCD (see xcd_tile)
+// write consecutive pieces of the same output rows (columns of x): its code
+// and scale bytes leave as longer runs, and the 16-byte scale pieces of one
+// 128-byte line meet in the L2. With a row copy too, row-major order does the
+// same for the row copy's half lines.
+template <bool kColMajor = false>
+__device__ __forceinline__ MfmaTile locate_mfma(int64_t tile, int64_t rows, int64_t cols) {
+  MfmaTile t;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if constexpr (kColMajor) {
+    const int64_t tiles_r = (rows + kTileRows - 1) / kTileRows;
+    t.tc = tile / tiles_r;
+    t.tr = tile - t.tc * tiles_r;
+  } else {
+    const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
+    t.tr = tile / tiles_c;
+    t.tc = tile - t.tr * tiles_c;
+  }
+  const int64_t wave_r0 = t.tr * kTileRows + 64 * wave;
+  const int64_t left = (rows - wave_r0) >> 4;  // whole steps left (rows % 16 == 0)
+  t.steps = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left >= kSteps ? kSteps : static_cast<int>(left)));
+  t.r0 = wave_r0 + 4 * (lane >> 4);
+  t.c0 = t.tc * kTileCols + 8 * (lane & 15);
+  t.col_valid = t.c0 < cols;
+  return t;
+}
+
+// raw[4 s + i] = the 8 bf16 of token r0 + 16 s + i, columns c0 .. c0 + 7,
+// for one step s (nontemporal). A step or columns past the matrix read the
+// matrix's first 8 values instead (every call has them), which are never
+// used, so every load goes out unconditionally.
+__device__ __forceinline__ void load_mfma_step(const uint16_t* __restrict__ x, int64_t ldx,
+                                               const MfmaTile& t, int s, uint4 (&raw)[16]) {
+  const bool ok = t.col_valid && s < t.steps;
+  const uint16_t* base = x + (ok ? (t.r0 + 16 * s) * ldx + t.c0 : 0);
+  const int64_t stride = ok ? ldx : 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[4 * s + i] = load_stream(base + i * stride);
+}
+
+__device__ __forceinline__ void load_mfma_raw(const uint16_t* __restrict__ x, int64_t ldx,
+                                              const MfmaTile& t, uint4 (&raw)[16]) {
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) load_mfma_step(x, ldx, t, s, raw);
+}
+
+// Tensor amax of the transformed tensor (and with kDual of the plain one),
+// as per-workgroup partial maxima. The amax needs only whole 16-token column
+// blocks, so its unit of work is shaped for the loads: a wave takes 32
+// tokens x 256 columns (two 16-token steps, two 128-column halves with the
+// MFMA lane layout), i.e. 512 contiguous bytes of each row where the
+// quantize tile reads 256, which streams at the full read rate. Waves walk
+// the units; as soon as a step and half is consumed, the same part of the
+// wave's next unit is requested into its registers.
+constexpr int kAmaxUnitRows = 32;
+constexpr int kAmaxUnitCols = 256;
+
+struct AmaxUnit {
+  int64_t r0;                // token of this lane's first row (step 0)
+  int64_t c0;                // first of this lane's 8 columns (half 0)
+  int steps;                 // steps inside the matrix (0..2), wave-uniform
+  bool valid0, valid1;       // the lane's columns exist in half 0 / 1
+};
+
+__device__ __forceinline__ AmaxUnit locate_amax_unit(int64_t u, int64_t rows, int64_t cols) {
+  AmaxUnit a;
+  const int lane = threadIdx.x & 63;
+  const int64_t units_c = (cols + kAmaxUnitCols - 1) / kAmaxUnitCols;
+  const int64_t ur = u / units_c, uc = u - ur * units_c;
+  const int64_t left = (rows - ur * kAmaxUnitRows) >> 4;
+  a.steps = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left >= 2 ? 2 : static_cast<int>(left)));
+  a.r0 = ur * kAmaxUnitRows + 4 * (lane >> 4);
+  a.c0 = uc * kAmaxUnitCols + 8 * (lane & 15);
+  a.valid0 = a.c0 < cols;
+  a.valid1 = a.c0 + 128 < cols;
+  return a;
+}
+
+// raw[4 (2 s + hc) + i] = token r0 + 16 s + i, columns c0 + 128 hc .. + 7;
+// parts past the matrix read its first 8 values (never used).
+__device__ __forceinline__ void load_amax_part(const uint16_t* __restrict__ x, int64_t ldx,
+                                               const AmaxUnit& a, int s, int hc, uint4 (&raw)[16]) {
+  const bool ok = (hc == 0 ? a.valid0 : a.valid1) && s < a.steps;
+  const uint16_t* base = x + (ok ? (a.r0 + 16 * s) * ldx + a.c0 + 128 * hc : 0);
+  const int64_t stride = ok ? ldx : 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[4 * (2 * s + hc) + i] = load_stream(base + i * stride);
+}
+
+template <bool kDual>
+__global__ __launch_bounds__(kThreads) void rht_amax_mfma_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, uint32_t sign_mask,
+    int64_t units, uint32_t* __restrict__ partials, uint32_t* __restrict__ partials_plain) {
+  __shared__ uint32_t lds4[kThreads / 64];
+  __shared__ uint32_t lds4_plain[kThreads / 64];
+  const bf16x4_t a = rht_a_operand(sign_mask);
+  float m = 0.0f;
+  uint32_t m_plain = 0;  // two packed 16-bit maxima of bf16 magnitudes
+  const int64_t wave_stride = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  int64_t u = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) +
+              __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  AmaxUnit cu = locate_amax_unit(u, rows, cols);
+  uint4 raw[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) load_amax_part(x, ldx, cu, q >> 1, q & 1, raw);
+  for (; u < units; u += wave_stride) {
+    const AmaxUnit uc = cu;
+    const bool has_next = u + wave_stride < units;
+    if (has_next) cu = locate_amax_unit(u + wave_stride, rows, cols);
+    float mt0 = 0.0f, mt1 = 0.0f;
+    uint32_t mp0 = 0, mp1 = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int s = q >> 1, hc = q & 1;
+      if (s < uc.steps) {
+        const uint4* rs = raw + 4 * q;
+        uint32_t mp = hc ? mp1 : mp0;
+        if constexpr (kDual) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            mp = max_u16x2(mp, rs[i].x & 0x7FFF7FFFu);
+            mp = max_u16x2(mp, rs[i].y & 0x7FFF7FFFu);
+            mp = max_u16x2(mp, rs[i].z & 0x7FFF7FFFu);
+            mp = max_u16x2(mp, rs[i].w & 0x7FFF7FFFu);
+          }
+        }
+        float mt = hc ? mt1 : mt0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4_t o[4];
+          if (h == 0) {
+            o[0] = rht_mfma<0>(a, rs);
+            o[1] = rht_mfma<1>(a, rs);
+            o[2] = rht_mfma<2>(a, rs);
+            o[3] = rht_mfma<3>(a, rs);
+          } else {
+            o[0] = rht_mfma<4>(a, rs);
+            o[1] = rht_mfma<5>(a, rs);
+            o[2] = rht_mfma<6>(a, rs);
+            o[3] = rht_mfma<7>(a, rs);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            mt = max3_abs(mt, o[j][0], o[j][1]);
+            mt = max3_abs(mt, o[j][2], o[j][3]);
+          }
+        }
+        if (hc) { mt1 = mt; mp1 = mp; } else { mt0 = mt; mp0 = mp; }
+      }
+      if (has_next) load_amax_part(x, ldx, cu, s, hc, raw);
+    }
+    // parts whose columns are past the matrix transformed placeholder data
+    if (uc.valid0) {
+      m = max_of(m, mt0);
+      if constexpr (kDual) m_plain = max_u16x2(m_plain, mp0);
+    }
+    if (uc.valid1) {
+      m = max_of(m, mt1);
+      if constexpr (kDual) m_plain = max_u16x2(m_plain, mp1);
+    }
+  }
+  block_max_store(__float_as_uint(m), lds4, partials + blockIdx.x);
+  if constexpr (kDual) {
+    const uint32_t lo = m_plain & 0xFFFFu, hi = m_plain >> 16;
+    block_max_store((lo > hi ? lo : hi) << 16, lds4_plain, partials_plain + blockIdx.x);
+  }
+}
+
+// Codes of one column pair of this lane (4 tokens each): column q0 in the
+// low 16 bits, q1 in the high ones (token i in nibble i of its half).
+// mult0 / mult1 are the columns' block multipliers (0 for a zero scale
+// byte, whose codes must be 0). For SR, wa / wb hold the random words of the
+// two columns' 4 tokens (token i: word i / 2, half i % 2).
+template <bool kSR>
+__device__ __forceinline__ uint32_t pair_codes(const f32x4_t& o0, const f32x4_t& o1, float mult0,
+                                               float mult1, uint32_t wa0, uint32_t wa1,
+                                               uint32_t wb0, uint32_t wb1) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    y[i] = __fmul_rn(o0[i], mult0);
+    y[4 + i] = __fmul_rn(o1[i], mult1);
+  }
+  uint32_t out;
+  if constexpr (kSR) {
+    out = pack8_sr(y, U4{wa0, wa1, wb0, wb1});
+  } else {
+    out = pack8_rn(y);
+  }
+  // a zero scale byte (multiplier 0) gives +-0 values, whose codes must be 0
+  const uint32_t keep = (mult0 != 0.0f ? 0x0000FFFFu : 0u) | (mult1 != 0.0f ? 0xFFFF0000u : 0u);
+  return out & keep;
+}
+
+// One workgroup per 256 x 128 tile: the Hadamard 16x1 column copy of bf16
+// x (tokens = rows), and with kDual the 1x16 round-to-nearest row copy from
+// the same loads. Field use as quantize_kernel's kModeRHT (no kDual) and
+// kModeRowRHT (kDual: the primary fields are the row copy's, the _t ones the
+// Hadamard copy's).
+template <bool kDual, bool kSR>
+__global__ __launch_bounds__(kThreads) void rht_quantize_mfma_kernel(QuantParams p) {
+  __shared__ __attribute__((aligned(16))) Staging st;
+  __shared__ float rtab_h[128];
+  __shared__ float rtab_r[kDual ? 128 : 1];
+  const int64_t rows = p.rows, cols = p.cols;
+  const int64_t ntiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
+  const MfmaTile t = locate_mfma<!kDual>(xcd_tile(static_cast<int64_t>(blockIdx.x), ntiles), rows, cols);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, r = lane >> 4;
+  const uint16_t* x = static_cast<const uint16_t*>(p.x);
+
+  // partial maxima first, then the tile: the reductions, the tables and the
+  // barrier wait only for the partials
+  const float* amax_in_h = kDual ? p.amax_in_t : p.amax_in;
+  const bool reduce_h = amax_in_h == nullptr;
+  const bool reduce_r = kDual && p.amax_in == nullptr;
+  PartialWords pw_h{}, pw_r{};
+  if (reduce_h) load_partials(kDual ? p.partials_t : p.partials, pw_h);
+  if (reduce_r) load_partials(p.partials, pw_r);
+  uint4 raw[16];
+  load_mfma_raw(x, p.ldx, t, raw);
+  const float amax_h = reduce_h ? reduce_loaded_partials(pw_h, p.n_partials) : *amax_in_h;
+  const float s_h = tensor_scale_from_amax(amax_h);
+  const ScaleDiv six_s_h = scale_div(__fmul_rn(6.0f, s_h));
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *(kDual ? p.tensor_scale_t : p.tensor_scale) = s_h;
+    float* out = kDual ? p.amax_out_t : p.amax_out;
+    if (out != nullptr) *out = amax_h;
+    if (!(amax_h <= 3.402823466e38f) && p.dev_status != nullptr) *p.dev_status = 1;
+  }
+  fill_recip_table(rtab_h, s_h);
+  ScaleDiv six_s_r = six_s_h;
+  if constexpr (kDual) {
+    const float amax_r = reduce_r ? reduce_loaded_partials(pw_r, p.n_partials) : *p.amax_in;
+    const float s_r = tensor_scale_from_amax(amax_r);
+    six_s_r = scale_div(__fmul_rn(6.0f, s_r));
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      *p.tensor_scale = s_r;
+      if (p.amax_out != nullptr) *p.amax_out = amax_r;
+      if (!(amax_r <= 3.402823466e38f) && p.dev_status != nullptr) *p.dev_status = 1;
+    }
+    fill_recip_table(rtab_r, s_r);
+  }
+  __syncthreads();
+
+  const bf16x4_t a = rht_a_operand(p.sign_mask);
+  const SrKey key = sr_key(p, kStreamCol);
+  const int c_local0 = 8 * n;
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    if (s >= t.steps) break;  // wave-uniform
+    const uint4* rs = raw + 4 * s;
+    const int tok_step = 64 * wave + 16 * s;  // tile-local first token of the step
+    if constexpr (kDual) {
+      if (t.col_valid) {
+        // 1x16 row blocks: this lane's 8 values of a token + lane ^ 1's 8
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w4[4] = {rs[i].x, rs[i].y, rs[i].z, rs[i].w};
+          float x8[8];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            x8[2 * k] = bf16_lo(w4[k]);
+            x8[2 * k + 1] = bf16_hi(w4[k]);
+          }
+          const float mine = abs_max<8>(x8);
+          const float am = fmaxf(mine, __uint_as_float(swap_adjacent_lanes(__float_as_uint(mine))));
+          const BlockMult bs = block_mult(am, six_s_r, rtab_r);
+          float y[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(x8[k], bs.mult);
+          const uint32_t w = pack8_rn(y) & ((bs.byte == 0u) ? 0u : 0xFFFFFFFFu);
+          const int64_t tok = t.r0 + 16 * s + i;
+          *reinterpret_cast<uint32_t*>(p.q_row + tok * (cols >> 1) + (t.c0 >> 1)) = w;
+          if ((n & 1) == 0) st.row_scales[(tok_step + 4 * r + i) * 8 + (n >> 1)] = static_cast<uint8_t>(bs.byte);
         }
       }
     }
-    if (out_col) {
-      // each column's codes for this tile's rows are contiguous in q_col: 8
-      // lanes write one column's 128 bytes as 16-byte granules (8-byte chunks
-      // when rows % 32 != 0 leaves column starts only 8-byte aligned), and its
-      // 16 scale bytes (1D) leave as one store where alignment allows
-      const int64_t rows_here = (rows - tr * kTileRows) < kTileRows ? (rows - tr * kTileRows) : kTileRows;
-      const int code_chunks = static_cast<int>(rows_here >> 4);  // 8-byte chunks per column
-      if ((rows & 31) == 0) {
-        const int granules = code_chunks >> 1;
+    // the Hadamard column copy, four columns at a time
 #pragma unroll
-        for (int k = tid; k < kTileCols * (kTileRows / 32); k += kThreads) {
-          const int c_local = k >> 3, g = k & 7;
-          const int64_t col = tc * kTileCols + c_local;
-          if (col < cols && g < granules) {
-            const uint4 val = *reinterpret_cast<const uint4*>(st.codes + staged_code_offset(c_local, 16 * g));
-            *reinterpret_cast<uint4*>(p.q_col + col * (rows >> 1) + tr * (kTileRows / 2) + 16 * g) = val;
-          }
+    for (int h = 0; h < 2; ++h) {
+      f32x4_t o[4];
+      o[0] = rht_mfma<0>(a, rs);
+      o[1] = rht_mfma<1>(a, rs);
+      o[2] = rht_mfma<2>(a, rs);
+      o[3] = rht_mfma<3>(a, rs);
+      if (h == 1) {
+        o[0] = rht_mfma<4>(a, rs);
+        o[1] = rht_mfma<5>(a, rs);
+        o[2] = rht_mfma<6>(a, rs);
+        o[3] = rht_mfma<7>(a, rs);
+      }
+      // block maxima over the columns' 4 lanes (rows r of the lane grid):
+      // after the two swaps, lane row r holds column {0, 2, 1, 3}[r] of the four
+      const auto s01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(col_absmax(o[0])),
+                                                        __float_as_uint(col_absmax(o[1])), false, false);
+      const auto s23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(col_absmax(o[2])),
+                                                        __float_as_uint(col_absmax(o[3])), false, false);
+      const float p01 = max_of(__uint_as_float(s01[0]), __uint_as_float(s01[1]));
+      const float p23 = max_of(__uint_as_float(s23[0]), __uint_as_float(s23[1]));
+      const auto sq = __builtin_amdgcn_permlane16_swap(__float_as_uint(p01), __float_as_uint(p23), false, false);
+      const float bmax = max_of(__uint_as_float(sq[0]), __uint_as_float(sq[1]));
+      const BlockMult bm = block_mult(bmax, six_s_h, rtab_h);
+      const int my_col = 4 * h + ((r & 1) << 1 | (r >> 1));  // {0, 2, 1, 3}[r] + 4 h
+      if (t.col_valid) st.col_scales[(c_local0 + my_col) * 16 + (tok_step >> 4)] = static_cast<uint8_t>(bm.byte);
+      // every lane needs the multipliers of all four columns
+      const uint32_t mb = __float_as_uint(bm.mult);
+      const auto u = __builtin_amdgcn_permlane16_swap(mb, mb, false, false);  // [c0 c0 c1 c1], [c2 c2 c3 c3]
+      const auto v01 = __builtin_amdgcn_permlane32_swap(u[0], u[0], false, false);
+      const auto v23 = __builtin_amdgcn_permlane32_swap(u[1], u[1], false, false);
+      const float mult[4] = {__uint_as_float(v01[0]), __uint_as_float(v01[1]), __uint_as_float(v23[0]),
+                             __uint_as_float(v23[1])};
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        // column pair (4 h + 2 pr, 4 h + 2 pr + 1); the lane grid's rows r and
+        // r ^ 1 hold tokens 0-3 and 4-7 of the same 8-token group
+        const int j0 = 4 * h + 2 * pr;
+        uint32_t wa0 = 0, wa1 = 0, wb0 = 0, wb1 = 0;
+        if constexpr (kSR) {
+          // the even row draws the group of column j0, the odd row that of
+          // j0 + 1; two swaps hand each lane the words of its 4 tokens
+          const uint64_t col = static_cast<uint64_t>(t.c0 + j0 + (r & 1));
+          const uint64_t tok8 = static_cast<uint64_t>(t.tr * kTileRows + tok_step + 8 * (r >> 1));
+          const uint64_t g = (col * static_cast<uint64_t>(rows) + tok8) >> 3;
+          const U4 w = words_for(key, g);
+          const auto e0 = __builtin_amdgcn_permlane16_swap(w.x, w.z, false, false);
+          const auto e1 = __builtin_amdgcn_permlane16_swap(w.y, w.w, false, false);
+          wa0 = e0[0];
+          wb0 = e0[1];
+          wa1 = e1[0];
+          wb1 = e1[1];
         }
-      } else {
-#pragma unroll
-        for (int k = tid; k < kTileCols * (kTileRows / 16); k += kThreads) {
-          const int c_local = k >> 4, ch = k & 15;
-          const int64_t col = tc * kTileCols + c_local;
-          if (col < cols && ch < code_chunks) {
-            const uint2 val = *reinterpret_cast<const uint2*>(st.codes + staged_code_offset(c_local, 8 * ch));
-            *reinterpret_cast<uint2*>(p.q_col + col * (rows >> 1) + tr * (kTileRows / 2) + ch * 8) = val;
-          }
+        const uint32_t codes = pair_codes<kSR>(o[2 * pr], o[2 * pr + 1], mult[2 * pr], mult[2 * pr + 1],
+                                               wa0, wa1, wb0, wb1);
+        // join rows r and r ^ 1: the even row takes column j0's 8 tokens, the
+        // odd row column j0 + 1's
+        const auto jn = __builtin_amdgcn_permlane16_swap(codes, codes, false, false);
+        const uint32_t dw = __builtin_amdgcn_perm(jn[1], jn[0], (r & 1) ? 0x07060302u : 0x05040100u);
+        if (t.col_valid) {
+          const int c_local = c_local0 + j0 + (r & 1);
+          *reinterpret_cast<uint32_t*>(st.codes + staged_code_offset(c_local, (tok_step >> 1) + 4 * (r >> 1))) = dw;
         }
       }
-      if constexpr (kMode != kMode2D) {
-        if (tid < kTileCols) {
-          const int64_t col = tc * kTileCols + tid;
-          if (col < cols) {
-            uint8_t* dst = p.s_col + col * (rows >> 4) + tr * (kTileRows / 16);
-            if (code_chunks == 16 && ((rows >> 4) & 15) == 0) {
-              *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(st.col_scales + tid * 16);
-            } else {
-              for (int b = 0; b < code_chunks; ++b) dst[b] = st.col_scales[tid * 16 + b];
-            }
-          }
-        }
+    }
+  }
+  __syncthreads();
+  store_staged(st, p, t.tr, t.tc, kDual, true, true);
+}
+
+// The transformed values of bf16 x, as the kernels above compute them.
+__global__ __launch_bounds__(kThreads) void rht_transform_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                      int64_t rows, int64_t cols,
+                                                                      int64_t ldx, uint32_t sign_mask,
+                                                                      float* __restrict__ out) {
+  const MfmaTile t = locate_mfma(blockIdx.x, rows, cols);
+  uint4 raw[16];
+  load_mfma_raw(x, ldx, t, raw);
+  const bf16x4_t a = rht_a_operand(sign_mask);
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    if (s >= t.steps) break;
+    const uint4* rs = raw + 4 * s;
+    f32x4_t o[8];
+    o[0] = rht_mfma<0>(a, rs);
+    o[1] = rht_mfma<1>(a, rs);
+    o[2] = rht_mfma<2>(a, rs);
+    o[3] = rht_mfma<3>(a, rs);
+    o[4] = rht_mfma<4>(a, rs);
+    o[5] = rht_mfma<5>(a, rs);
+    o[6] = rht_mfma<6>(a, rs);
+    o[7] = rht_mfma<7>(a, rs);
+    if (t.col_valid) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4* dst = reinterpret_cast<float4*>(out + (t.r0 + 16 * s + i) * cols + t.c0);
+        dst[0] = make_float4(o[0][i], o[1][i], o[2][i], o[3][i]);
+        dst[1] = make_float4(o[4][i], o[5][i], o[6][i], o[7][i]);
       }
     }
   }
@@ -852,7 +1391,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QuantParams p) 
   __syncthreads();
   const float amax = amax_lds;
   const float s = tensor_scale_from_amax(amax);
-  const float six_s = __fmul_rn(6.0f, s);
+  const ScaleDiv six_s = scale_div(__fmul_rn(6.0f, s));
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
     *p.tensor_scale = s;
     if (p.amax_out != nullptr) *p.amax_out = amax;
@@ -864,6 +1403,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QuantParams p) 
 
   // rows of 16 * even values keep 16-byte code and 2-byte scale stores aligned
   const bool wide_stores = (nblk_row & 1) == 0;
+  const SrKey key = sr_key(p, kStreamRow);
   for (; row < rows; row += row_step) {
     Chunk<InT> nxt;
     const int64_t next = row + row_step;
@@ -881,8 +1421,8 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QuantParams p) 
       if constexpr (kSR) {
         const uint64_t g = (static_cast<uint64_t>(row) * static_cast<uint64_t>(cols) +
                             static_cast<uint64_t>(c0 + 16 * b)) >> 3;
-        w[2 * b] = pack8_sr(y, sr_words(p.k0, p.k1, g, p.offset, kStreamRow));
-        w[2 * b + 1] = pack8_sr(y + 8, sr_words(p.k0, p.k1, g + 1, p.offset, kStreamRow));
+        w[2 * b] = pack8_sr(y, words_for(key, g));
+        w[2 * b + 1] = pack8_sr(y + 8, words_for(key, g + 1));
       } else {
         w[2 * b] = pack8_rn(y);
         w[2 * b + 1] = pack8_rn(y + 8);
@@ -939,6 +1479,13 @@ int64_t amax_workgroups(int64_t rows, int64_t cols, int64_t ldx, bool rht, int64
     const int64_t g = (n + per_block - 1) / per_block;
     return g > kMaxPartials ? kMaxPartials : g;
   }
+  if (rht && elem_bytes == 2) {
+    // rht_amax_mfma_kernel: one wave per 32 x 256 unit, walking
+    const int64_t units = ((rows + kAmaxUnitRows - 1) / kAmaxUnitRows) *
+                          ((cols + kAmaxUnitCols - 1) / kAmaxUnitCols);
+    const int64_t g = (units + kThreads / 64 - 1) / (kThreads / 64);
+    return g < kMaxTileBlocks ? g : kMaxTileBlocks;
+  }
   const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
   return tiles < kMaxTileBlocks ? tiles : kMaxTileBlocks;
 }
@@ -956,7 +1503,18 @@ int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
     const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
     const unsigned gg = static_cast<unsigned>(g);
     const bool ragged = (rows % 16) != 0;
-    if (rht && dual) {
+    if (rht && sizeof(InT) == 2) {
+      const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+      const int64_t units = ((rows + kAmaxUnitRows - 1) / kAmaxUnitRows) *
+                            ((cols + kAmaxUnitCols - 1) / kAmaxUnitCols);
+      if (dual) {
+        rht_amax_mfma_kernel<true><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask, units,
+                                                                partials, partials_plain);
+      } else {
+        rht_amax_mfma_kernel<false><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask,
+                                                                 units, partials, nullptr);
+      }
+    } else if (rht && dual) {
       amax_tile_kernel<InT, true, false, true><<<gg, kThreads, 0, stream>>>(
           x, rows, cols, ldx, sign_mask, tiles, partials, partials_plain);
     } else if (rht) {
@@ -975,16 +1533,40 @@ int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
 
 // The tile kernel serves every call with a column copy or 16x16 blocks; those
 // require rows % 16 == 0 (ragged row counts reach only the row-copy kernel).
+template <bool kDual, bool kSR>
+void launch_rht_mfma(const QuantParams& p, hipStream_t stream) {
+  const int64_t tiles =
+      ((p.rows + kTileRows - 1) / kTileRows) * ((p.cols + kTileCols - 1) / kTileCols);
+  rht_quantize_mfma_kernel<kDual, kSR><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(p);
+}
+
 template <typename InT>
 void dispatch_quant(const QuantParams& p, int mode, bool sr, hipStream_t stream) {
+  if constexpr (sizeof(InT) == 2) {
+    // bf16 Hadamard paths: the transform on the matrix cores
+    if (mode == kModeRHT) {
+      if (sr) launch_rht_mfma<false, true>(p, stream);
+      else launch_rht_mfma<false, false>(p, stream);
+      return;
+    }
+    if (mode == kModeRowRHT) {
+      if (sr) launch_rht_mfma<true, true>(p, stream);
+      else launch_rht_mfma<true, false>(p, stream);
+      return;
+    }
+  }
   if (mode == kMode2D) {
     launch_quant<InT, kMode2D, false>(p, stream);
   } else if (mode == kModeRHT) {
-    if (sr) launch_quant<InT, kModeRHT, true>(p, stream);
-    else launch_quant<InT, kModeRHT, false>(p, stream);
+    if constexpr (sizeof(InT) == 4) {
+      if (sr) launch_quant<InT, kModeRHT, true>(p, stream);
+      else launch_quant<InT, kModeRHT, false>(p, stream);
+    }
   } else if (mode == kModeRowRHT) {
-    if (sr) launch_quant<InT, kModeRowRHT, true>(p, stream);
-    else launch_quant<InT, kModeRowRHT, false>(p, stream);
+    if constexpr (sizeof(InT) == 4) {
+      if (sr) launch_quant<InT, kModeRowRHT, true>(p, stream);
+      else launch_quant<InT, kModeRowRHT, false>(p, stream);
+    }
   } else {
     if (sr) launch_quant<InT, kMode1D, true>(p, stream);
     else launch_quant<InT, kMode1D, false>(p, stream);
@@ -1119,7 +1701,7 @@ int launch_rht_transform(const void* x, bool x_bf16, int64_t tokens, int64_t col
   if (tokens == 0 || cols == 0) return 0;
   const int64_t tiles = ((tokens + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
   if (x_bf16) {
-    rht_transform_kernel<uint16_t><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(
+    rht_transform_mfma_kernel<<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(x), tokens, cols, ldx, sign_mask, out);
   } else {
     rht_transform_kernel<float><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(

@@ -230,6 +230,26 @@ def test_rn_sweep_of_ties_through_the_kernel():
     check_against_oracle(x, "fp32", outputs=("row",))
 
 
+@pytest.mark.parametrize("k", [-75, -60, -53, -50, -20, 0, 40, 100])
+def test_block_scale_division_across_tensor_scales(k):
+    """The same tensor scaled by 2^k (exactly) through every quantizer mode:
+    the kernels divide block maxima by 6 S with a reciprocal and one
+    correction step where 6 S >= 2^-60 (|x| up to about 2^-52 and above),
+    and with an IEEE division below; both must give the oracle's bytes."""
+    x = (wl.activation(528, 400, seed=31) * np.float32(2.0 ** k)).astype(np.float32)
+    assert np.all(np.isfinite(x))
+    announce(f"division 2^{k}")
+    check_against_oracle(x, "fp32")
+    check_against_oracle(x, "fp32", rounding="sr", seed=3, offset=1, outputs=("row",))
+    for dtype in ("fp32", "bf16"):
+        xb = x if dtype == "fp32" else wl.to_bf16_values(x)
+        row, col, _ = run_quantize(xb, dtype, block=1, outputs=3)
+        ref = o.quantize_2d(xb)
+        assert np.array_equal(host(row.scales), ref["row"].scales)
+        assert np.array_equal(host(row.codes), ref["row"].codes)
+        assert np.array_equal(host(col.codes), ref["col"].codes)
+
+
 def test_zero_tiny_and_empty_tensors():
     torch = require_gpu()
     import bit_block_scaled_bf16_amd as nv

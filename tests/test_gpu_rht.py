@@ -88,6 +88,24 @@ def test_quantization_of_transformed_values_bit_exact(shape, rounding):
     assert np.array_equal(host(q.codes), ref.codes)
 
 
+@pytest.mark.parametrize("k", [-70, -55, 0, 60])
+def test_quantization_bit_exact_across_tensor_scales(k):
+    """bf16 input scaled by 2^k: the transform scales exactly, and the block
+    scales (reciprocal and correction step, or IEEE division for tiny tensor
+    scales) must still equal the oracle's on the kernel's transformed values."""
+    announce(f"rht quantize scaled 2^{k}")
+    x = wl.to_bf16_values(wl.activation(272, 400, seed=12) * np.float32(2.0 ** k))
+    for rounding in (0, 1):
+        q, ws = run_rht_quantize(x, "bf16", rounding, seed=7, offset=2)
+        xt_gpu = gpu_transform(x, "bf16", 7)
+        assert host(ws)[0] == np.float32(np.max(np.abs(xt_gpu)))
+        ref = o.quantize(xt_gpu, rounding="rn" if rounding == 0 else "sr", seed=7, offset=2,
+                         outputs=("col",))["col"]
+        assert host(q.tensor_scale)[0] == ref.tensor_scale
+        assert np.array_equal(host(q.scales), ref.scales)
+        assert np.array_equal(host(q.codes), ref.codes)
+
+
 @pytest.mark.parametrize("rounding", ["rn", "sr"])
 def test_end_to_end_against_oracle(rounding):
     x = wl.laplace((1024, 512), seed=8)
