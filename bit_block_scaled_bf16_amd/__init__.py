@@ -37,6 +37,8 @@ from ._lib import (  # noqa: F401  (re-exported constants and raw entry points)
     nvfp4_rht_quantize,
     nvfp4_rht_sign_mask,
     nvfp4_rht_transform,
+    nvfp4_stream_copy,
+    nvfp4_stream_read,
     mxfp4_dequantize,
     mxfp4_gemm,
     mxfp4_quantize,

@@ -49,12 +49,16 @@ _SIGNATURES = {
     "fp8_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P, _P, _P]),
     "fp8_dequantize": (_INT, [_P, _P, _I64, _I64, _INT, _P, _I64, _P]),
     "fp8_gemm": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _I64, _P]),
+    "nvfp4_stream_read": (_INT, [_P, _I64, _P, _P]),
+    "nvfp4_stream_copy": (_INT, [_P, _P, _I64, _P]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
 
 # Bytes of the amax workspace (NVFP4_AMAX_WS_BYTES in include/nvfp4.h).
 AMAX_WS_BYTES = 16384
+# Words of nvfp4_stream_read's checksum buffer (NVFP4_STREAM_SINK_WORDS).
+STREAM_SINK_WORDS = 1024
 
 _lib = None
 
@@ -232,3 +236,15 @@ def nvfp4_rht_transform(x, rht_seed, out, stream=None) -> None:
 
 def nvfp4_rht_sign_mask(rht_seed: int) -> int:
     return int(lib().nvfp4_rht_sign_mask(rht_seed))
+
+
+def nvfp4_stream_read(src, nbytes, sink, stream=None) -> None:
+    if sink.numel() * sink.element_size() < 4 * STREAM_SINK_WORDS:
+        raise ValueError(f"stream_read sink must hold {STREAM_SINK_WORDS} uint32")
+    _check("nvfp4_stream_read", lib().nvfp4_stream_read(_ptr(src), nbytes, _ptr(sink),
+                                                        _stream(stream)))
+
+
+def nvfp4_stream_copy(src, dst, nbytes, stream=None) -> None:
+    _check("nvfp4_stream_copy", lib().nvfp4_stream_copy(_ptr(src), _ptr(dst), nbytes,
+                                                        _stream(stream)))

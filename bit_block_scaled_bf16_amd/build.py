@@ -22,7 +22,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libnvfp4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["abi.cpp", "quantize.hip", "dequant.hip", "gemm.hip", "mxfp4.hip", "fp8.hip", "f8f6f4_gemm.hip", "noalloc.hip"]
+SOURCES = ["abi.cpp", "quantize.hip", "dequant.hip", "gemm.hip", "mxfp4.hip", "fp8.hip", "f8f6f4_gemm.hip", "noalloc.hip",
+           "stream.hip"]
 
 # -ffp-contract=off: the quantizer's float32 steps are single roundings each
 #   (no fused multiply-add), as the format definition requires.

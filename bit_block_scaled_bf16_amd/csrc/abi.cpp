@@ -425,6 +425,25 @@ int fp8_gemm(const uint8_t* qa, const float* ta, const uint8_t* qb, const float*
              : NVFP4_ERR_HIP;
 }
 
+int nvfp4_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes < 0 || (bytes % 16) != 0) return NVFP4_ERR_SHAPE;
+  if (bytes == 0) return NVFP4_OK;
+  if (src == nullptr || sink == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return NVFP4_ERR_ALIGN;
+  return nvfp4::launch_stream_read(src, bytes, sink, stream) > 0 ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+int nvfp4_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  if (bytes < 0 || (bytes % 16) != 0) return NVFP4_ERR_SHAPE;
+  if (bytes == 0) return NVFP4_OK;
+  if (src == nullptr || dst == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return NVFP4_ERR_ALIGN;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + static_cast<uintptr_t>(bytes) && b < a + static_cast<uintptr_t>(bytes))
+    return NVFP4_ERR_SHAPE;  // overlapping buffers
+  return nvfp4::launch_stream_copy(src, dst, bytes, stream) == 0 ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
 }  // extern "C"
 
 namespace nvfp4 {

@@ -102,6 +102,11 @@ int launch_philox_fill(uint64_t seed, uint32_t c2, uint32_t c3, int64_t n_groups
 int launch_rht_transform(const void* x, bool x_bf16, int64_t tokens, int64_t cols, int64_t ldx,
                          uint32_t sign_mask, float* out, hipStream_t stream);
 
+// Streaming references (stream.hip). launch_stream_read returns the number
+// of checksum words written (workgroups), or -1 on a launch error.
+int launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+int launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 // Host-side Philox4x32-10 (same definition as the device function).
 void philox4x32_10_host(uint32_t k0, uint32_t k1, const uint32_t ctr[4], uint32_t out[4]);
 

@@ -43,6 +43,8 @@ KERNEL_SOURCES = {
     "quantize_kernel": "quantize.hip",
     "amax_flat_kernel": "quantize.hip",
     "amax_tile_kernel": "quantize.hip",
+    "rht_amax_mfma_kernel": "quantize.hip",
+    "rht_quantize_mfma_kernel": "quantize.hip",
     "mxfp4": "mxfp4.hip",
     "fp8": "fp8.hip",
     "f8f6f4_gemm": "f8f6f4_gemm.hip",
@@ -52,8 +54,13 @@ KERNEL_SOURCES = {
 
 
 def source_hash(fname: str) -> str:
-    with open(os.path.join(CSRC, fname), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 of a kernel source together with the library's shared headers
+    (csrc/*.h), so that a change to either invalidates its figures."""
+    h = hashlib.sha256()
+    for name in [fname] + sorted(n for n in os.listdir(CSRC) if n.endswith(".h")):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def short_name(name: str) -> str:
@@ -149,6 +156,11 @@ def counters_summary(run_dir: str, out_md: str, command: str) -> None:
         "VALU inst/wave | MFMA inst/wave |",
         "|---|---|---|---|---|---|---|---|---|",
     ]
+    result = {
+        "command": command,
+        "sources": {k: source_hash(v) for k, v in sorted(set(KERNEL_SOURCES.items()))},
+        "kernels": {},
+    }
     for d in sorted(agg):
         name, us = meta[d]
         if "Fill" in name or "copyBuffer" in name or CALIBRATION_KERNEL in name:
@@ -164,8 +176,14 @@ def counters_summary(run_dir: str, out_md: str, command: str) -> None:
         lines.append(f"| {d} | `{name}` | {us:.1f} | {clk:.2f} | {mfma:.3f} | {mfma * clk / 2.4:.3f} | "
                      f"{valu:.2f} | {c['SQ_INSTS_VALU'] / waves:.0f} | "
                      f"{c['SQ_INSTS_MFMA'] / waves:.0f} |")
+        result["kernels"].setdefault(name, []).append({
+            "us": round(us, 1), "clock_ghz": round(clk, 3), "mfma_busy": round(mfma, 4),
+            "mfma_peak_share": round(mfma * clk / 2.4, 4), "valu_busy": round(valu, 4),
+            "valu_inst_per_wave": round(c["SQ_INSTS_VALU"] / waves, 1),
+            "mfma_inst_per_wave": round(c["SQ_INSTS_MFMA"] / waves, 1)})
+    lines += ["", "```json", json.dumps(result, indent=1), "```", ""]
     with open(out_md, "w") as f:
-        f.write("\n".join(lines) + "\n")
+        f.write("\n".join(lines))
 
 
 def traffic_summary(fetch_dir: str, write_dir: str, copy_bytes: int, out_md: str,
@@ -226,12 +244,37 @@ def traffic_summary(fetch_dir: str, write_dir: str, copy_bytes: int, out_md: str
 
 
 def load_traffic(md_path: str):
-    """The JSON block of a traffic summary, or None."""
+    """The JSON block of a traffic or counters summary, or None."""
     if not os.path.exists(md_path):
         return None
     text = open(md_path).read()
     m = re.search(r"```json\n(.*?)\n```", text, re.S)
     return json.loads(m.group(1)) if m else None
+
+
+def _sources_current(data, source_key) -> bool:
+    for key in (source_key,) if isinstance(source_key, str) else source_key:
+        src = KERNEL_SOURCES.get(key)
+        if src is None or data["sources"].get(key) != source_hash(src):
+            return False
+    return True
+
+
+def kernel_counters(md_path: str, kernels, source_key):
+    """Busy fractions of one call's kernels from a counters summary: a dict
+    short-name fragment -> that dispatch's clock, MFMA / VALU busy and
+    instructions per wave. None when the summary is missing, has none of the
+    kernels, or the source of source_key changed since it was taken."""
+    data = load_traffic(md_path)
+    if data is None or not _sources_current(data, source_key):
+        return None
+    out = {}
+    for frag, idx in kernels:
+        for name, rows in data["kernels"].items():
+            if frag in name and idx < len(rows):
+                out[frag.rstrip(",")] = rows[idx]
+                break
+    return out or None
 
 
 def kernel_traffic(md_path: str, kernels, source_key):
@@ -241,12 +284,8 @@ def kernel_traffic(md_path: str, kernels, source_key):
     summary is missing, none of the kernels is in it, or the source of
     source_key (one key or a tuple of keys) changed since it was taken."""
     data = load_traffic(md_path)
-    if data is None:
+    if data is None or not _sources_current(data, source_key):
         return None
-    for key in (source_key,) if isinstance(source_key, str) else source_key:
-        src = KERNEL_SOURCES.get(key)
-        if src is None or data["sources"].get(key) != source_hash(src):
-            return None
     total, found = 0, False
     for frag, idx in kernels:
         for name, d in data["kernels"].items():

@@ -370,6 +370,31 @@ int fp8_dequantize(const uint8_t* q, const float* tensor_scale, int64_t rows, in
 int fp8_gemm(const uint8_t* qa, const float* ta, const uint8_t* qb, const float* tb, int64_t M,
              int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Streaming references (measurement, not part of the format): plain
+ * hand-written streams over device memory, 16-byte nontemporal loads, 8 per
+ * thread in flight, timed beside the quantizers to show the read and copy
+ * rates the memory system gives a kernel with no arithmetic.
+ * ------------------------------------------------------------------------ */
+
+/* Words of the checksum buffer of nvfp4_stream_read. */
+#define NVFP4_STREAM_SINK_WORDS 1024
+
+/*
+ * nvfp4_stream_read -- reads bytes of src (bytes % 16 == 0, src 16-byte
+ * aligned) and writes the XOR of the 32-bit words each workgroup read into
+ * sink[0 .. g), g = min(NVFP4_STREAM_SINK_WORDS, ceil(bytes / 32768)); sink
+ * holds NVFP4_STREAM_SINK_WORDS uint32. The XOR of sink[0 .. g) is the XOR of
+ * all 32-bit words of src. bytes == 0 writes nothing.
+ */
+int nvfp4_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
+/*
+ * nvfp4_stream_copy -- dst[0 .. bytes) = src[0 .. bytes) (bytes % 16 == 0,
+ * both 16-byte aligned, not overlapping).
+ */
+int nvfp4_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -122,6 +122,20 @@ def test_quantize_noalloc_argument_errors(L):
     assert n(q_row=MIS) == 4
 
 
+def test_stream_reference_argument_errors(L):
+    assert L.nvfp4_stream_read(FAKE, 24, FAKE, None) == 2      # bytes % 16
+    assert L.nvfp4_stream_read(FAKE, -16, FAKE, None) == 2
+    assert L.nvfp4_stream_read(None, 64, FAKE, None) == 1
+    assert L.nvfp4_stream_read(FAKE, 64, None, None) == 1
+    assert L.nvfp4_stream_read(MIS, 64, FAKE, None) == 4
+    assert L.nvfp4_stream_read(FAKE, 0, None, None) == 0        # nothing to read
+    assert L.nvfp4_stream_copy(FAKE, FAKE + 4096, 40, None) == 2
+    assert L.nvfp4_stream_copy(FAKE, None, 64, None) == 1
+    assert L.nvfp4_stream_copy(FAKE, MIS + 4096, 64, None) == 4
+    assert L.nvfp4_stream_copy(FAKE, FAKE + 32, 64, None) == 2  # overlapping
+    assert L.nvfp4_stream_copy(FAKE, FAKE, 0, None) == 0
+
+
 def test_rht_quantize_argument_errors(L):
     def r(**kw):
         a = dict(x=FAKE, x_dtype=1, tokens=32, cols=32, ldx=32, rht_seed=7, rounding=1, seed=7,
