@@ -1097,15 +1097,25 @@ __global__ __launch_bounds__(kThreads) void rht_amax_mfma_kernel(
   }
 }
 
+// v kept in a register as it is: the compiler can no longer recompute it
+// from its inputs at each use (which it otherwise does for cheap lane
+// values, at a cost of several instructions per use in the loops below).
+template <typename T>
+__device__ __forceinline__ T pinned(T v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
 // Codes of one column pair of this lane (4 tokens each): column q0 in the
 // low 16 bits, q1 in the high ones (token i in nibble i of its half).
 // mult0 / mult1 are the columns' block multipliers (0 for a zero scale
 // byte, whose codes must be 0). For SR, wa / wb hold the random words of the
 // two columns' 4 tokens (token i: word i / 2, half i % 2).
+// any_zero (wave-uniform) says whether a multiplier of the wave is 0.
 template <bool kSR>
 __device__ __forceinline__ uint32_t pair_codes(const f32x4_t& o0, const f32x4_t& o1, float mult0,
                                                float mult1, uint32_t wa0, uint32_t wa1,
-                                               uint32_t wb0, uint32_t wb1) {
+                                               uint32_t wb0, uint32_t wb1, bool any_zero) {
   float y[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1119,8 +1129,12 @@ __device__ __forceinline__ uint32_t pair_codes(const f32x4_t& o0, const f32x4_t&
     out = pack8_rn(y);
   }
   // a zero scale byte (multiplier 0) gives +-0 values, whose codes must be 0
-  const uint32_t keep = (mult0 != 0.0f ? 0x0000FFFFu : 0u) | (mult1 != 0.0f ? 0xFFFF0000u : 0u);
-  return out & keep;
+  if (any_zero) {
+    asm volatile("");  // keeps this a branch: not to be computed on every call
+    const uint32_t keep = (mult0 != 0.0f ? 0x0000FFFFu : 0u) | (mult1 != 0.0f ? 0xFFFF0000u : 0u);
+    out &= keep;
+  }
+  return out;
 }
 
 // One workgroup per 256 x 128 tile: the Hadamard 16x1 column copy of bf16
@@ -1128,7 +1142,9 @@ __device__ __forceinline__ uint32_t pair_codes(const f32x4_t& o0, const f32x4_t&
 // the same loads. Field use as quantize_kernel's kModeRHT (no kDual) and
 // kModeRowRHT (kDual: the primary fields are the row copy's, the _t ones the
 // Hadamard copy's).
-template <bool kDual, bool kSR>
+// kWideG: group indices can exceed 32 bits (rows x cols >= 2^35), which
+// takes the general Philox counter instead of the 32-bit one.
+template <bool kDual, bool kSR, bool kWideG>
 __global__ __launch_bounds__(kThreads) void rht_quantize_mfma_kernel(QuantParams p) {
   __shared__ __attribute__((aligned(16))) Staging st;
   __shared__ float rtab_h[128];
@@ -1177,6 +1193,25 @@ __global__ __launch_bounds__(kThreads) void rht_quantize_mfma_kernel(QuantParams
   const bf16x4_t a = rht_a_operand(p.sign_mask);
   const SrKey key = sr_key(p, kStreamCol);
   const int c_local0 = 8 * n;
+  // Lane constants of the loop below. The Philox group of column c and
+  // tokens t..t+7 is g = (c rows + t) / 8 = c rows / 8 + t / 8 (rows is a
+  // multiple of 16), so each (step, column pair) adds a launch constant to
+  // this lane's first group (column c0 + (r & 1), token 8 (r >> 1) of the
+  // wave's first step).
+  const uint64_t rows8 = static_cast<uint64_t>(rows) >> 3;
+  const uint64_t g_lane = pinned(static_cast<uint64_t>(t.c0 + (r & 1)) * rows8 +
+                                 static_cast<uint64_t>(t.tr * (kTileRows / 8) + 8 * wave + (r >> 1)));
+  const uint32_t join_sel = pinned((r & 1) ? 0x07060302u : 0x05040100u);
+  // st.col_scales index of this lane's column {0, 2, 1, 3}[r] (+ 4 h) and
+  // step s: this base + 64 h + s
+  const int scale_lane = pinned((c_local0 + ((r & 1) << 1 | (r >> 1))) * 16 + 4 * wave);
+  // staged_code_offset(c_local0 + j0 + (r & 1), 32 wave + 8 s + 4 (r >> 1))
+  // for j0 < 8 and s < 4: the column's granule swizzle is n & 7 and the
+  // granule index 2 wave + (s >> 1), so the offset is one of two lane bases
+  // plus 128 j0 + 8 (s & 1).
+  const int lds_lane = (c_local0 + (r & 1)) * kLdsCodeStride + 4 * (r >> 1);
+  const int lds_swz = ((2 * wave) ^ (n & 7)) << 4;
+  const int lds_half[2] = {pinned(lds_lane + lds_swz), pinned(lds_lane + (lds_swz ^ 16))};
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     if (s >= t.steps) break;  // wave-uniform
@@ -1232,10 +1267,13 @@ __global__ __launch_bounds__(kThreads) void rht_quantize_mfma_kernel(QuantParams
       const auto sq = __builtin_amdgcn_permlane16_swap(__float_as_uint(p01), __float_as_uint(p23), false, false);
       const float bmax = max_of(__uint_as_float(sq[0]), __uint_as_float(sq[1]));
       const BlockMult bm = block_mult(bmax, six_s_h, rtab_h);
-      const int my_col = 4 * h + ((r & 1) << 1 | (r >> 1));  // {0, 2, 1, 3}[r] + 4 h
-      if (t.col_valid) st.col_scales[(c_local0 + my_col) * 16 + (tok_step >> 4)] = static_cast<uint8_t>(bm.byte);
+      // column {0, 2, 1, 3}[r] + 4 h of this lane's eight
+      if (t.col_valid) st.col_scales[scale_lane + 64 * h + s] = static_cast<uint8_t>(bm.byte);
       // every lane needs the multipliers of all four columns
       const uint32_t mb = __float_as_uint(bm.mult);
+      // a zero multiplier (zero scale byte) anywhere in the wave: rare, so
+      // its code masking runs behind a uniform branch
+      const bool any_zero = __builtin_amdgcn_ballot_w64(bm.mult == 0.0f) != 0;
       const auto u = __builtin_amdgcn_permlane16_swap(mb, mb, false, false);  // [c0 c0 c1 c1], [c2 c2 c3 c3]
       const auto v01 = __builtin_amdgcn_permlane32_swap(u[0], u[0], false, false);
       const auto v23 = __builtin_amdgcn_permlane32_swap(u[1], u[1], false, false);
@@ -1250,10 +1288,13 @@ __global__ __launch_bounds__(kThreads) void rht_quantize_mfma_kernel(QuantParams
         if constexpr (kSR) {
           // the even row draws the group of column j0, the odd row that of
           // j0 + 1; two swaps hand each lane the words of its 4 tokens
-          const uint64_t col = static_cast<uint64_t>(t.c0 + j0 + (r & 1));
-          const uint64_t tok8 = static_cast<uint64_t>(t.tr * kTileRows + tok_step + 8 * (r >> 1));
-          const uint64_t g = (col * static_cast<uint64_t>(rows) + tok8) >> 3;
-          const U4 w = words_for(key, g);
+          const uint64_t g = g_lane + static_cast<uint64_t>(j0) * rows8 + static_cast<uint64_t>(2 * s);
+          U4 w;
+          if constexpr (kWideG) {
+            w = sr_words(key.k0, key.k1, g, key.offset, key.stream);
+          } else {
+            w = sr_words_fast(key.ps, static_cast<uint32_t>(g));
+          }
           const auto e0 = __builtin_amdgcn_permlane16_swap(w.x, w.z, false, false);
           const auto e1 = __builtin_amdgcn_permlane16_swap(w.y, w.w, false, false);
           wa0 = e0[0];
@@ -1262,14 +1303,13 @@ __global__ __launch_bounds__(kThreads) void rht_quantize_mfma_kernel(QuantParams
           wb1 = e1[1];
         }
         const uint32_t codes = pair_codes<kSR>(o[2 * pr], o[2 * pr + 1], mult[2 * pr], mult[2 * pr + 1],
-                                               wa0, wa1, wb0, wb1);
+                                               wa0, wa1, wb0, wb1, any_zero);
         // join rows r and r ^ 1: the even row takes column j0's 8 tokens, the
         // odd row column j0 + 1's
         const auto jn = __builtin_amdgcn_permlane16_swap(codes, codes, false, false);
-        const uint32_t dw = __builtin_amdgcn_perm(jn[1], jn[0], (r & 1) ? 0x07060302u : 0x05040100u);
+        const uint32_t dw = __builtin_amdgcn_perm(jn[1], jn[0], join_sel);
         if (t.col_valid) {
-          const int c_local = c_local0 + j0 + (r & 1);
-          *reinterpret_cast<uint32_t*>(st.codes + staged_code_offset(c_local, (tok_step >> 1) + 4 * (r >> 1))) = dw;
+          *reinterpret_cast<uint32_t*>(st.codes + lds_half[s >> 1] + j0 * kLdsCodeStride + 8 * (s & 1)) = dw;
         }
       }
     }
@@ -1537,7 +1577,13 @@ template <bool kDual, bool kSR>
 void launch_rht_mfma(const QuantParams& p, hipStream_t stream) {
   const int64_t tiles =
       ((p.rows + kTileRows - 1) / kTileRows) * ((p.cols + kTileCols - 1) / kTileCols);
-  rht_quantize_mfma_kernel<kDual, kSR><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(p);
+  if constexpr (kSR) {
+    if (static_cast<uint64_t>(p.rows) * static_cast<uint64_t>(p.cols) >= (uint64_t(1) << 35)) {
+      rht_quantize_mfma_kernel<kDual, true, true><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(p);
+      return;
+    }
+  }
+  rht_quantize_mfma_kernel<kDual, kSR, false><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(p);
 }
 
 template <typename InT>
