@@ -33,8 +33,13 @@ __device__ __forceinline__ float tensor_scale_from_amax(float amax) {
 // (checked against the CPU definition for every float32 near every E4M3
 // value and midpoint).
 __device__ __forceinline__ uint32_t e4m3_from_float(float t) {
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(t, 448.0f), 0.0f, 0,
-                                                               false)) & 0xFFu;
+  // t >= 0, whose bits order like its value: an integer minimum clamps it
+  // (a NaN's bits lie above 448's, so a NaN clamps to 448 as with fminf)
+  const uint32_t tb = __float_as_uint(t);
+  const float c = __uint_as_float(tb < 0x43E00000u ? tb : 0x43E00000u);
+  // old value 0 and second value +0, whose E4M3 byte is 0: bytes 1..3 of
+  // the result are 0
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false));
 }
 
 // Value of an E4M3FN byte b in 0x00..0x7E, branch-free: b << 20 places the

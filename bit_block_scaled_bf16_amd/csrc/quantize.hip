@@ -47,6 +47,7 @@ __device__ __forceinline__ int staged_code_offset(int col, int byte) {
   return col * kLdsCodeStride + ((((byte >> 4) ^ ((col >> 3) & 7)) << 4) | (byte & 15));
 }
 constexpr int64_t kMaxTileBlocks = 1024;  // workgroups of the tile-shaped amax kernels
+constexpr int64_t kInfinityCacheBytes = int64_t(256) << 20;  // MI355X's memory-side cache
 
 // kModeRowRHT: the 1x16 row copy (round to nearest) and the Hadamard column
 // copy of the same tensor, each with its own tensor scale, from one read.
@@ -197,12 +198,26 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// An ordinary (cache-allocating) 16-byte load: the amax pass uses it when
+// the quantize pass that follows can find the input still in the Infinity
+// Cache.
+__device__ __forceinline__ uint4 load_keep(const void* p) { return *static_cast<const uint4*>(p); }
+
+template <bool kKeep>
+__device__ __forceinline__ uint4 load_amax(const void* p) {
+  if constexpr (kKeep) {
+    return load_keep(p);
+  } else {
+    return load_stream(p);
+  }
+}
+
 __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, a),
                                                                 __builtin_bit_cast(ushort2_t, b)));
 }
 
-template <typename InT>
+template <typename InT, bool kKeep>
 __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* __restrict__ x, int64_t n,
                                                              uint32_t* __restrict__ partials) {
   __shared__ uint32_t lds4[kThreads / 64];
@@ -217,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* __restri
 #pragma unroll
     for (int u = 0; u < kFlatUnroll; ++u) {
       const int64_t i = base + u * kThreads;
-      r[u] = i < nvec ? load_stream(xv + i) : make_uint4(0u, 0u, 0u, 0u);
+      r[u] = i < nvec ? load_amax<kKeep>(xv + i) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < kFlatUnroll; ++u) {
@@ -985,6 +1000,7 @@ __device__ __forceinline__ void load_mfma_raw(const uint16_t* __restrict__ x, in
 // wave's next unit is requested into its registers.
 constexpr int kAmaxUnitRows = 32;
 constexpr int kAmaxUnitCols = 256;
+constexpr int64_t kAmaxUnitsPerBlock = 20;
 
 struct AmaxUnit {
   int64_t r0;                // token of this lane's first row (step 0)
@@ -1009,16 +1025,17 @@ __device__ __forceinline__ AmaxUnit locate_amax_unit(int64_t u, int64_t rows, in
 
 // raw[4 (2 s + hc) + i] = token r0 + 16 s + i, columns c0 + 128 hc .. + 7;
 // parts past the matrix read its first 8 values (never used).
+template <bool kKeep>
 __device__ __forceinline__ void load_amax_part(const uint16_t* __restrict__ x, int64_t ldx,
                                                const AmaxUnit& a, int s, int hc, uint4 (&raw)[16]) {
   const bool ok = (hc == 0 ? a.valid0 : a.valid1) && s < a.steps;
   const uint16_t* base = x + (ok ? (a.r0 + 16 * s) * ldx + a.c0 + 128 * hc : 0);
   const int64_t stride = ok ? ldx : 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) raw[4 * (2 * s + hc) + i] = load_stream(base + i * stride);
+  for (int i = 0; i < 4; ++i) raw[4 * (2 * s + hc) + i] = load_amax<kKeep>(base + i * stride);
 }
 
-template <bool kDual>
+template <bool kDual, bool kKeep>
 __global__ __launch_bounds__(kThreads) void rht_amax_mfma_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, uint32_t sign_mask,
     int64_t units, uint32_t* __restrict__ partials, uint32_t* __restrict__ partials_plain) {
@@ -1033,7 +1050,7 @@ __global__ __launch_bounds__(kThreads) void rht_amax_mfma_kernel(
   AmaxUnit cu = locate_amax_unit(u, rows, cols);
   uint4 raw[16];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) load_amax_part(x, ldx, cu, q >> 1, q & 1, raw);
+  for (int q = 0; q < 4; ++q) load_amax_part<kKeep>(x, ldx, cu, q >> 1, q & 1, raw);
   for (; u < units; u += wave_stride) {
     const AmaxUnit uc = cu;
     const bool has_next = u + wave_stride < units;
@@ -1078,7 +1095,7 @@ __global__ __launch_bounds__(kThreads) void rht_amax_mfma_kernel(
         }
         if (hc) { mt1 = mt; mp1 = mp; } else { mt0 = mt; mp0 = mp; }
       }
-      if (has_next) load_amax_part(x, ldx, cu, s, hc, raw);
+      if (has_next) load_amax_part<kKeep>(x, ldx, cu, s, hc, raw);
     }
     // parts whose columns are past the matrix transformed placeholder data
     if (uc.valid0) {
@@ -1212,6 +1229,9 @@ __global__ __launch_bounds__(kThreads) void rht_quantize_mfma_kernel(QuantParams
   const int lds_lane = (c_local0 + (r & 1)) * kLdsCodeStride + 4 * (r >> 1);
   const int lds_swz = ((2 * wave) ^ (n & 7)) << 4;
   const int lds_half[2] = {pinned(lds_lane + lds_swz), pinned(lds_lane + (lds_swz ^ 16))};
+  // st.row_scales index of this lane's tokens (row copy, even lanes):
+  // this base + 8 (16 s + i) for token i of step s
+  const int row_scale_lane = pinned((64 * wave + 4 * r) * 8 + (n >> 1));
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     if (s >= t.steps) break;  // wave-uniform
@@ -1229,16 +1249,21 @@ __global__ __launch_bounds__(kThreads) void rht_quantize_mfma_kernel(QuantParams
             x8[2 * k] = bf16_lo(w4[k]);
             x8[2 * k + 1] = bf16_hi(w4[k]);
           }
-          const float mine = abs_max<8>(x8);
-          const float am = fmaxf(mine, __uint_as_float(swap_adjacent_lanes(__float_as_uint(mine))));
-          const BlockMult bs = block_mult(am, six_s_r, rtab_r);
+          // magnitudes: their bits order like their values
+          const uint32_t mine = __float_as_uint(abs_max<8>(x8));
+          const uint32_t other = swap_adjacent_lanes(mine);
+          const BlockMult bs = block_mult(__uint_as_float(mine > other ? mine : other), six_s_r, rtab_r);
           float y[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(x8[k], bs.mult);
-          const uint32_t w = pack8_rn(y) & ((bs.byte == 0u) ? 0u : 0xFFFFFFFFu);
+          uint32_t w = pack8_rn(y);
+          if (__builtin_amdgcn_ballot_w64(bs.byte == 0u) != 0) {
+            asm volatile("");  // a rare branch: zero scale bytes, whose codes must be 0
+            w = (bs.byte == 0u) ? 0u : w;
+          }
           const int64_t tok = t.r0 + 16 * s + i;
           *reinterpret_cast<uint32_t*>(p.q_row + tok * (cols >> 1) + (t.c0 >> 1)) = w;
-          if ((n & 1) == 0) st.row_scales[(tok_step + 4 * r + i) * 8 + (n >> 1)] = static_cast<uint8_t>(bs.byte);
+          if ((n & 1) == 0) st.row_scales[row_scale_lane + (16 * s + i) * 8] = static_cast<uint8_t>(bs.byte);
         }
       }
     }
@@ -1520,10 +1545,13 @@ int64_t amax_workgroups(int64_t rows, int64_t cols, int64_t ldx, bool rht, int64
     return g > kMaxPartials ? kMaxPartials : g;
   }
   if (rht && elem_bytes == 2) {
-    // rht_amax_mfma_kernel: one wave per 32 x 256 unit, walking
+    // rht_amax_mfma_kernel: waves walk 32 x 256 units; about 20 units per
+    // workgroup (5 per wave) measured faster than one unit per wave for the
+    // 16384 x 5120 activation (2048 waves against 4096), and large tensors
+    // keep kMaxTileBlocks workgroups
     const int64_t units = ((rows + kAmaxUnitRows - 1) / kAmaxUnitRows) *
                           ((cols + kAmaxUnitCols - 1) / kAmaxUnitCols);
-    const int64_t g = (units + kThreads / 64 - 1) / (kThreads / 64);
+    const int64_t g = (units + kAmaxUnitsPerBlock - 1) / kAmaxUnitsPerBlock;
     return g < kMaxTileBlocks ? g : kMaxTileBlocks;
   }
   const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
@@ -1532,13 +1560,17 @@ int64_t amax_workgroups(int64_t rows, int64_t cols, int64_t ldx, bool rht, int64
 
 template <typename InT>
 int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
-                uint32_t sign_mask, float* amax_ws, hipStream_t stream, bool dual = false) {
+                uint32_t sign_mask, float* amax_ws, hipStream_t stream, bool dual = false,
+                bool keep = false) {
   uint32_t* partials = reinterpret_cast<uint32_t*>(amax_ws) + kPartialsOffset;
   uint32_t* partials_plain = partials + kMaxPartials;
   const int64_t g = amax_workgroups(rows, cols, ldx, rht, sizeof(InT));
   if (!rht && ldx == cols) {
-    amax_flat_kernel<InT><<<static_cast<unsigned>(g), kThreads, 0, stream>>>(x, rows * cols,
-                                                                             partials);
+    if (keep) {
+      amax_flat_kernel<InT, true><<<static_cast<unsigned>(g), kThreads, 0, stream>>>(x, rows * cols, partials);
+    } else {
+      amax_flat_kernel<InT, false><<<static_cast<unsigned>(g), kThreads, 0, stream>>>(x, rows * cols, partials);
+    }
   } else {
     const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
     const unsigned gg = static_cast<unsigned>(g);
@@ -1547,12 +1579,18 @@ int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
       const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
       const int64_t units = ((rows + kAmaxUnitRows - 1) / kAmaxUnitRows) *
                             ((cols + kAmaxUnitCols - 1) / kAmaxUnitCols);
-      if (dual) {
-        rht_amax_mfma_kernel<true><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask, units,
-                                                                partials, partials_plain);
+      if (dual && keep) {
+        rht_amax_mfma_kernel<true, true><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask, units,
+                                                                      partials, partials_plain);
+      } else if (dual) {
+        rht_amax_mfma_kernel<true, false><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask, units,
+                                                                       partials, partials_plain);
+      } else if (keep) {
+        rht_amax_mfma_kernel<false, true><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask,
+                                                                       units, partials, nullptr);
       } else {
-        rht_amax_mfma_kernel<false><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask,
-                                                                 units, partials, nullptr);
+        rht_amax_mfma_kernel<false, false><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask,
+                                                                        units, partials, nullptr);
       }
     } else if (rht && dual) {
       amax_tile_kernel<InT, true, false, true><<<gg, kThreads, 0, stream>>>(
@@ -1680,10 +1718,20 @@ int launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
   p.amax_out_t = nullptr;
   p.tensor_scale_t = q.tensor_scale_t;
   if (q.amax_in == nullptr) {
+    // Infinity Cache residency: when the input and what the quantize pass
+    // writes (codes and 1D scales, 9/16 byte per element and copy) fit in
+    // the 256 MiB cache together, the amax pass reads with allocating loads
+    // and the quantize pass finds the input there; otherwise both passes
+    // stream with nontemporal loads (measured: a 168 MB activation's
+    // one-call pair gains about 4 us, a 210 MB weight's 16x16 pair loses
+    // about 8 us with allocating loads)
+    const int64_t elems = q.rows * q.cols;
+    const int64_t copies = dual ? 2 : (q.rht ? 1 : ((q.outputs & 1) != 0) + ((q.outputs & 2) != 0));
+    const bool keep = elems * (bf16 ? 2 : 4) + copies * (elems / 2 + elems / 16) <= kInfinityCacheBytes;
     const int n = bf16 ? launch_amax(static_cast<const uint16_t*>(q.x), q.rows, q.cols, q.ldx,
-                                     q.rht, q.sign_mask, q.amax_ws, stream, dual)
+                                     q.rht, q.sign_mask, q.amax_ws, stream, dual, keep)
                        : launch_amax(static_cast<const float*>(q.x), q.rows, q.cols, q.ldx,
-                                     q.rht, q.sign_mask, q.amax_ws, stream, dual);
+                                     q.rht, q.sign_mask, q.amax_ws, stream, dual, keep);
     if (n < 0) return -1;
     const uint32_t* base = reinterpret_cast<const uint32_t*>(q.amax_ws) + kPartialsOffset;
     p.n_partials = n;
