@@ -27,6 +27,9 @@ int check_input(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
 // Tensors larger than this are split by the caller (the kernels index tiles
 // with 32-bit grid coordinates).
 constexpr int64_t kMaxElements = int64_t(1) << 40;
+// Rows of either operand of the MXFP4 and FP8 GEMMs (their loads index rows
+// with 32-bit integers).
+constexpr int64_t kMaxBlockGemmRows = int64_t(1) << 30;
 
 // The argument checks of nvfp4_quantize; fills q when they pass. With
 // ws_required, amax_ws must be given when amax_in is not (the no-allocation
@@ -343,6 +346,7 @@ int mxfp4_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const ui
                hipStream_t stream) {
   if (!valid_dtype(c_dtype)) return NVFP4_ERR_ENUM;
   if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || ldc < N) return NVFP4_ERR_SHAPE;
+  if (M > kMaxBlockGemmRows || N > kMaxBlockGemmRows) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (M > kMaxElements / N || (K > 0 && (M > kMaxElements / K || N > kMaxElements / K)))
     return NVFP4_ERR_SHAPE;
@@ -411,6 +415,7 @@ int fp8_gemm(const uint8_t* qa, const float* ta, const uint8_t* qb, const float*
              int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc, hipStream_t stream) {
   if (!valid_dtype(c_dtype)) return NVFP4_ERR_ENUM;
   if (M < 0 || N < 0 || K < 0 || (K % 64) != 0 || ldc < N) return NVFP4_ERR_SHAPE;
+  if (M > kMaxBlockGemmRows || N > kMaxBlockGemmRows) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (M > kMaxElements / N || (K > 0 && (M > kMaxElements / K || N > kMaxElements / K)))
     return NVFP4_ERR_SHAPE;

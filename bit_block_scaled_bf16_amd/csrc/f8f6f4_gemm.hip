@@ -65,7 +65,9 @@ struct Traits<Fmt::kMxFp4> {
   static constexpr int kSub = 4;                    // MFMA sub-steps (K = 64) per step
   static constexpr int kChunks = 1;                 // 16-byte chunks per lane and fragment
   static constexpr int kScaleRow = kBK / kMxBlock;  // scale bytes per row and step
-  static constexpr int kScaleBytes = kTile * kScaleRow;
+  static constexpr int kChunkSteps = 4;             // steps per scale chunk
+  static constexpr int kChunkRow = kChunkSteps * kScaleRow;
+  static constexpr int kChunkBytes = kTile * kChunkRow;  // per operand
   static __device__ __forceinline__ int64_t row_bytes(int64_t K) { return K >> 1; }
 };
 
@@ -75,18 +77,24 @@ struct Traits<Fmt::kFp8> {
   static constexpr int kSub = 2;
   static constexpr int kChunks = 2;
   static constexpr int kScaleRow = 0;
-  static constexpr int kScaleBytes = 0;
+  static constexpr int kChunkSteps = 1;
+  static constexpr int kChunkRow = 0;
+  static constexpr int kChunkBytes = 0;
   static __device__ __forceinline__ int64_t row_bytes(int64_t K) { return K; }
 };
 
-// LDS: [A codes, stages 0 and 1][B codes][A scales][B scales].
+// LDS: [A codes, stages 0 and 1][B codes][scale buffer 0: A, B][buffer 1]
+// (160 KiB for MXFP4). A scale buffer holds a chunk of 4 steps' scale bytes
+// (32 per row): loading 8 rows' 32 bytes per instruction instead of 32
+// rows' 8 bytes per step touches a quarter as many lines per step.
 template <Fmt F>
 struct Lds {
   static constexpr int kA = 0;
   static constexpr int kB = 2 * kCodeBytes;
   static constexpr int kSa = 4 * kCodeBytes;
-  static constexpr int kSb = kSa + 2 * Traits<F>::kScaleBytes;
-  static constexpr int kBytes = kSb + 2 * Traits<F>::kScaleBytes;
+  static constexpr int kSb = kSa + Traits<F>::kChunkBytes;
+  static constexpr int kScaleBuf = 2 * Traits<F>::kChunkBytes;  // between the two buffers
+  static constexpr int kBytes = kSa + 2 * kScaleBuf;
 };
 
 typedef int int8v_t __attribute__((ext_vector_type(8)));
@@ -100,18 +108,18 @@ struct BlockGemmParams {
 
 // One operand's loads for this wave: 8 code loads of 8 rows each (lane j of
 // load k: tile row 64 w + 8 k + j / 8, the chunk whose swizzled slot is
-// j % 8) and, for MXFP4, 2 scale loads of 32 rows (lane j: row
-// 64 w + 32 k + j / 2, the 4 bytes (j % 2) of the row's 8 bytes of the step).
-// (row >> 1) & 7 = (4 k + j / 16) & 7 for these rows, so the chunk depends
-// on k only through k % 2, and load k is load k % 2 plus 8 k rows. Rows past
-// the matrix read its last row instead (they only feed C outside M x N).
+// j % 8) and, for MXFP4, scale loads of 8 rows each (lane j: the same row,
+// 4 bytes of the row's scale chunk). (row >> 1) & 7 = (4 k + j / 16) & 7 for
+// these rows. Rows past the matrix read its last row instead (they only feed
+// C outside M x N). Addresses are formed with integer minimums, not
+// selects: a select on a pointer can become a branch, and a branch in the
+// loop let the compiler sink the MFMAs behind the loads.
 struct Dma {
-  const uint8_t* rowp;   // this lane's row of load 0 (unclamped)
-  const uint8_t* lastp;  // the matrix's last row (uniform)
-  const uint8_t* srowp;  // this lane's scale row of scale load 0 (MXFP4; unclamped)
-  const uint8_t* slastp; // the last scale row (uniform)
-  int left, sleft;       // rows from load 0's (scale load 0's) row to the end of the matrix
-  int64_t rb, srb;       // code and scale bytes per row (uniform)
+  const uint8_t* q;  // operand codes (uniform)
+  const uint8_t* s;  // operand scales (uniform; MXFP4)
+  int row;          // this lane's row of load 0
+  int last;         // the operand's last row
+  int64_t rb, srb;   // code and scale bytes per row (uniform)
 };
 
 __device__ __forceinline__ int dma_chunk(int k, int lane) { return (lane & 7) ^ ((4 * k + (lane >> 4)) & 7); }
@@ -120,63 +128,107 @@ template <Fmt F>
 __device__ __forceinline__ Dma dma_setup(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
                                          int64_t row0, int64_t rows, int64_t K, int wave, int lane) {
   Dma d;
+  d.q = q;
+  d.s = s;
   d.rb = Traits<F>::row_bytes(K);
   d.srb = K / kMxBlock;
-  const int64_t row = row0 + 64 * wave + (lane >> 3);
-  const int64_t srow = row0 + 64 * wave + (lane >> 1);
-  // rows - row, capped: only its comparison with the tile's row offsets matters
-  d.left = static_cast<int>((rows - row) < kTile ? (rows - row) : kTile);
-  d.sleft = static_cast<int>((rows - srow) < kTile ? (rows - srow) : kTile);
-  d.rowp = q + row * d.rb;
-  d.lastp = q + (rows - 1) * d.rb;
-  d.srowp = nullptr;
-  d.slastp = nullptr;
-  if constexpr (F == Fmt::kMxFp4) {
-    d.srowp = s + srow * d.srb + 4 * (lane & 1);
-    d.slastp = s + (rows - 1) * d.srb + 4 * (lane & 1);
-  }
+  d.row = static_cast<int>(row0) + 64 * wave + (lane >> 3);
+  d.last = static_cast<int>(rows) - 1;
   return d;
 }
 
-// Requests step `step` of one operand (this wave's 64 rows) into the LDS
-// stage at byte addresses codes / scales. A half step (64 bytes per row, the
-// last step of some K) reads chunk c & 3 for chunk c and the row's first 4
-// scale bytes for both scale words: the slots of chunks 4-7 and the second
-// scale word then hold copies that are never read.
+// Requests step `step` of one operand's codes (this wave's 64 rows) into the
+// LDS stage at byte address codes. A half step (64 bytes per row, the last
+// step of some K) reads chunk c & 3 for chunk c: the slots of chunks 4-7
+// then hold copies that are never read.
 template <Fmt F>
-__device__ __forceinline__ void dma_step(const Dma& d, uint32_t codes, uint32_t scales, int step,
-                                         bool half, int wave, int lane) {
+__device__ __forceinline__ void dma_step(const Dma& d, uint32_t codes, int step, bool half, int wave,
+                                         int lane) {
   const int64_t off = static_cast<int64_t>(step) * kRowBytes;
   const uint32_t c0 = codes + 64 * wave * kRowBytes;
+  const int cmask = half ? 3 : 7;
 #pragma unroll
   for (int k = 0; k < kDmaLoads; ++k) {
-    const int c = dma_chunk(k, lane) & (half ? 3 : 7);
-    const uint8_t* g = (8 * k < d.left) ? d.rowp + (8 * k) * d.rb : d.lastp;
-    lds_dma<16>(g + off + 16 * c, c0 + k * (8 * kRowBytes));
-  }
-  if constexpr (F == Fmt::kMxFp4) {
-    const int64_t soff = static_cast<int64_t>(step) * Traits<F>::kScaleRow;
-    const uint32_t s0 = scales + 64 * wave * Traits<F>::kScaleRow;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint8_t* g = (32 * k < d.sleft) ? d.srowp + (32 * k) * d.srb : d.slastp;
-      const int back = (lane & 1) * (half ? 4 : 0);
-      lds_dma<4>(g + soff - back, s0 + k * (32 * Traits<F>::kScaleRow));
-    }
+    const int row = min(d.row + 8 * k, d.last);
+    const int c = dma_chunk(k, lane) & cmask;
+    lds_dma<16>(d.q + static_cast<int64_t>(row) * d.rb + off + 16 * c, c0 + k * (8 * kRowBytes));
   }
 }
 
-// Step `step` of A and B into stage step % 2; a half step when step is the
-// last and K leaves half a step (uniform choice).
+// Step `step` of A's and B's codes into stage step % 2; a half step when
+// step is the last and K leaves half a step.
 template <Fmt F>
 __device__ __forceinline__ void dma_both(const Dma& da, const Dma& db, uint32_t lds, int step, bool half,
                                          int wave, int lane) {
   using L = Lds<F>;
   const int st = step & 1;
-  const uint32_t ca = lds + L::kA + st * kCodeBytes, sa = lds + L::kSa + st * Traits<F>::kScaleBytes;
-  const uint32_t cb = lds + L::kB + st * kCodeBytes, sb = lds + L::kSb + st * Traits<F>::kScaleBytes;
-  dma_step<F>(da, ca, sa, step, half, wave, lane);
-  dma_step<F>(db, cb, sb, step, half, wave, lane);
+  dma_step<F>(da, lds + L::kA + st * kCodeBytes, step, half, wave, lane);
+  dma_step<F>(db, lds + L::kB + st * kCodeBytes, step, half, wave, lane);
+}
+
+// Quarter q (loads 2q and 2q + 1, 16 rows of this wave's 64) of scale chunk
+// `chunk` (MXFP4) of one operand into the LDS buffer at byte address buf:
+// lane j of load k carries bytes 4 (j % 8) .. + 3 of the chunk's 32 bytes of
+// row 64 w + 8 k + j / 8. Bytes past the row's K / 32 (the last chunk of a K
+// that is not a multiple of 1024) read the row's first bytes instead.
+__device__ __forceinline__ void dma_scale_quarter(const Dma& d, uint32_t buf, int chunk, int q, int wave,
+                                                  int lane) {
+  constexpr int kRow = Traits<Fmt::kMxFp4>::kChunkRow;
+  const int64_t want = static_cast<int64_t>(chunk) * kRow + 4 * (lane & 7);
+  const int64_t off = want + 4 <= d.srb ? want : 0;  // past the row's end: its first bytes
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int r = 16 * q + 8 * e;  // load 2 q + e: rows r .. r + 7 of the wave's 64
+    const int row = min(d.row + r, d.last);
+    lds_dma<4>(d.s + static_cast<int64_t>(row) * d.srb + off, buf + (64 * wave + r) * kRow);
+  }
+}
+
+__device__ __forceinline__ void dma_scales(const Dma& da, const Dma& db, uint32_t lds, int chunk, int q,
+                                           int wave, int lane) {
+  using L = Lds<Fmt::kMxFp4>;
+  const uint32_t buf = (chunk & 1) * L::kScaleBuf;
+  dma_scale_quarter(da, lds + L::kSa + buf, chunk, q, wave, lane);
+  dma_scale_quarter(db, lds + L::kSb + buf, chunk, q, wave, lane);
+}
+
+// Single loads, for interleaving with the MFMAs. A step's loads of one
+// operand are the 8 code loads k and, for MXFP4, the two loads e of one
+// quarter of a scale chunk; "part 0" of a step's loads is A's codes 0-3,
+// B's codes 0-3 and A's scale loads, "part 1" the rest (B's scale loads).
+template <Fmt F>
+__device__ __forceinline__ void dma_code(const Dma& d, uint32_t operand, int step, bool half, int k, int wave,
+                                         int lane) {
+  const int st = step & 1;
+  const int row = min(d.row + 8 * k, d.last);
+  const int c = dma_chunk(k, lane) & (half ? 3 : 7);
+  lds_dma<16>(d.q + static_cast<int64_t>(row) * d.rb + static_cast<int64_t>(step) * kRowBytes + 16 * c,
+              operand + st * kCodeBytes + (64 * wave + 8 * k) * kRowBytes);
+}
+
+__device__ __forceinline__ void dma_scale(const Dma& d, uint32_t operand, int chunk, int q, int e, int wave,
+                                          int lane) {
+  using L = Lds<Fmt::kMxFp4>;
+  constexpr int kRow = Traits<Fmt::kMxFp4>::kChunkRow;
+  const int64_t want = static_cast<int64_t>(chunk) * kRow + 4 * (lane & 7);
+  const int64_t off = want + 4 <= d.srb ? want : 0;  // past the row's end: its first bytes
+  const int r = 16 * q + 8 * e;
+  const int row = min(d.row + r, d.last);
+  lds_dma<4>(d.s + static_cast<int64_t>(row) * d.srb + off, operand + (chunk & 1) * L::kScaleBuf + (64 * wave + r) * kRow);
+}
+
+template <int kN>
+using IC = std::integral_constant<int, kN>;
+
+template <typename Fn, int... kI>
+__device__ __forceinline__ void unroll_impl(Fn&& fn, std::integer_sequence<int, kI...>) {
+  (fn(IC<kI>{}), ...);
+}
+
+// fn(IC<0>{}), ..., fn(IC<kN - 1>{}) in order.
+template <int kN, typename Fn>
+__device__ __forceinline__ void unroll(Fn&& fn) {
+  unroll_impl(fn, std::make_integer_sequence<int, kN>{});
 }
 
 // One sub-step's fragments, each the MFMA operand of one row (column)
@@ -210,8 +262,8 @@ __device__ __forceinline__ FragOffsets frag_offsets(int wm, int wn, int lane, bo
     o.a[q] = L::kA + ra * kRowBytes + 16 * (c ^ swz);
     o.b[q] = L::kB + rb * kRowBytes + 16 * (c ^ swz);
   }
-  o.sa = L::kSa + ra * Traits<F>::kScaleRow + (half ? 2 * h : 4 * h);
-  o.sb = L::kSb + rb * Traits<F>::kScaleRow + (half ? 2 * h : 4 * h);
+  o.sa = L::kSa + ra * Traits<F>::kChunkRow + (half ? 2 * h : 4 * h);
+  o.sb = L::kSb + rb * Traits<F>::kChunkRow + (half ? 2 * h : 4 * h);
   return o;
 }
 
@@ -240,26 +292,64 @@ __device__ __forceinline__ void read_frags(Frags<F>& f, const uint8_t* __restric
   }
 }
 
-// The lane's scale words of a step (MXFP4): one 32-bit word per block of a
-// full step, one 16-bit half of a half step.
+// Fragment n (A 0-3, then B 0-3) of sub-step kSubStep of stage st.
+template <Fmt F, int kSubStep, int kN>
+__device__ __forceinline__ void read_frag(Frags<F>& f, const uint8_t* __restrict__ lds, const FragOffsets& o,
+                                          int st) {
+  constexpr int kC = Traits<F>::kChunks, i = kN & 3;
+  const int* off = kN < 4 ? o.a : o.b;
+  const uint8_t* p = lds + st * kCodeBytes + i * 32 * kRowBytes;
+  const uint4 v0 = *reinterpret_cast<const uint4*>(p + off[kSubStep * kC]);
+  typename Frags<F>::Frag v;
+  if constexpr (kC == 2) {
+    const uint4 v1 = *reinterpret_cast<const uint4*>(p + off[kSubStep * kC + 1]);
+    v = int8v_t{static_cast<int>(v0.x), static_cast<int>(v0.y), static_cast<int>(v0.z), static_cast<int>(v0.w),
+                static_cast<int>(v1.x), static_cast<int>(v1.y), static_cast<int>(v1.z), static_cast<int>(v1.w)};
+  } else {
+    v = v0;
+  }
+  if constexpr (kN < 4) {
+    f.a[i] = v;
+  } else {
+    f.b[i] = v;
+  }
+}
+
+// The lane's scale words of step `step` (MXFP4): one 32-bit word per block
+// of a full step, one 16-bit half of a half step.
 template <bool kHalf>
 __device__ __forceinline__ void read_scales(uint32_t (&sa)[4], uint32_t (&sb)[4], const uint8_t* __restrict__ lds,
-                                            const FragOffsets& o, int st) {
-  constexpr int kRow = Traits<Fmt::kMxFp4>::kScaleRow, kBytes = Traits<Fmt::kMxFp4>::kScaleBytes;
+                                            const FragOffsets& o, int step) {
+  using T = Traits<Fmt::kMxFp4>;
+  const int soff = ((step / T::kChunkSteps) & 1) * Lds<Fmt::kMxFp4>::kScaleBuf + (step % T::kChunkSteps) * T::kScaleRow;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (kHalf) {
-      sa[i] = *reinterpret_cast<const uint16_t*>(lds + o.sa + st * kBytes + i * 32 * kRow);
-      sb[i] = *reinterpret_cast<const uint16_t*>(lds + o.sb + st * kBytes + i * 32 * kRow);
+      sa[i] = *reinterpret_cast<const uint16_t*>(lds + o.sa + soff + i * 32 * T::kChunkRow);
+      sb[i] = *reinterpret_cast<const uint16_t*>(lds + o.sb + soff + i * 32 * T::kChunkRow);
     } else {
-      sa[i] = *reinterpret_cast<const uint32_t*>(lds + o.sa + st * kBytes + i * 32 * kRow);
-      sb[i] = *reinterpret_cast<const uint32_t*>(lds + o.sb + st * kBytes + i * 32 * kRow);
+      sa[i] = *reinterpret_cast<const uint32_t*>(lds + o.sa + soff + i * 32 * T::kChunkRow);
+      sb[i] = *reinterpret_cast<const uint32_t*>(lds + o.sb + soff + i * 32 * T::kChunkRow);
     }
   }
 }
 
 // An FP4 operand: 16 bytes in the low half of the operand tuple (the
 // instruction reads 4 registers for FP4).
+// Scale word n (A blocks 0-3, then B) of step `step` (MXFP4, full step).
+template <int kN>
+__device__ __forceinline__ void read_scale_word(uint32_t (&sa)[4], uint32_t (&sb)[4], const uint8_t* __restrict__ lds,
+                                                const FragOffsets& o, int step, IC<kN>) {
+  using T = Traits<Fmt::kMxFp4>;
+  const int soff = ((step / T::kChunkSteps) & 1) * Lds<Fmt::kMxFp4>::kScaleBuf + (step % T::kChunkSteps) * T::kScaleRow;
+  constexpr int i = kN & 3;
+  if constexpr (kN < 4) {
+    sa[i] = *reinterpret_cast<const uint32_t*>(lds + o.sa + soff + i * 32 * T::kChunkRow);
+  } else {
+    sb[i] = *reinterpret_cast<const uint32_t*>(lds + o.sb + soff + i * 32 * T::kChunkRow);
+  }
+}
+
 __device__ __forceinline__ int8v_t operand16(const uint4& v) {
   return int8v_t{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z),
                  static_cast<int>(v.w), 0, 0, 0, 0};
@@ -289,6 +379,39 @@ __device__ __forceinline__ void mfma_substep(floatx16_t (&acc)[4][4], const Frag
             kFmtE4M3, 0, kScaleOne, 0, kScaleOne);
       }
     }
+}
+
+// MFMA n (= 4 i + j) of a sub-step.
+template <Fmt F, int kSel, int kN>
+__device__ __forceinline__ void mfma_one(floatx16_t (&acc)[4][4], const Frags<F>& f, const uint32_t (&sa)[4],
+                                         const uint32_t (&sb)[4]) {
+  constexpr int i = kN >> 2, j = kN & 3;
+  if constexpr (F == Fmt::kMxFp4) {
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(operand16(f.b[j]), operand16(f.a[i]), acc[i][j],
+                                                                kFmtE2M1, kFmtE2M1, kSel, static_cast<int>(sb[j]),
+                                                                kSel, static_cast<int>(sa[i]));
+  } else {
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], kFmtE4M3, kFmtE4M3, 0,
+                                                                kScaleOne, 0, kScaleOne);
+  }
+}
+
+// A sub-step's 16 MFMAs with kActions other instructions spread over them:
+// action a (act(IC<a>)) follows MFMA (16 a) / kActions. Scheduling fences
+// keep this order: loads issued in one burst stall the wave's instruction
+// stream (the address unit's queue fills) while the matrix unit idles.
+template <Fmt F, int kSel, int kActions, typename Act>
+__device__ __forceinline__ void substep(floatx16_t (&acc)[4][4], const Frags<F>& f, const uint32_t (&sa)[4],
+                                        const uint32_t (&sb)[4], Act&& act) {
+  unroll<16>([&](auto n_c) {
+    constexpr int n = decltype(n_c)::value;
+    mfma_one<F, kSel, n>(acc, f, sa, sb);
+    unroll<kActions>([&](auto a_c) {
+      constexpr int a = decltype(a_c)::value;
+      if constexpr ((16 * a) / kActions == n) act(a_c);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  });
 }
 
 // s_waitcnt immediate: at most n vector memory loads outstanding (vmcnt is
@@ -327,15 +450,25 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(BlockGemmParams
   const Dma db = dma_setup<F>(p.qb, p.sb, n0, p.N, K, wave_u, lane);
   const FragOffsets o = frag_offsets<F>(wm, wn, lane, false);
 
-  // prologue: steps 0 and 1 into stages 0 and 1; step 0 must have landed
+  // prologue: steps 0 and 1 into stages 0 and 1 (step 0 again when it is
+  // the only one), scale chunks 0 and 1 (0 again when it is the only one);
+  // step 0 and chunk 0 must have landed
+  const int nchunks = (nsteps + T::kChunkSteps - 1) / T::kChunkSteps;
   dma_both<F>(da, db, lds0, 0, nfull == 0, wave_u, lane);
-  if (nsteps > 1) {
-    dma_both<F>(da, db, lds0, 1, nfull == 1, wave_u, lane);
-    constexpr int kDma = 2 * (kDmaLoads + (F == Fmt::kMxFp4 ? 2 : 0));
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(kDma));
-  } else {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if constexpr (F == Fmt::kMxFp4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma_scales(da, db, lds0, 0, q, wave_u, lane);
   }
+  {
+    const int s1 = nsteps > 1 ? 1 : 0;
+    dma_both<F>(da, db, lds0, s1, s1 == nfull, wave_u, lane);
+  }
+  if constexpr (F == Fmt::kMxFp4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma_scales(da, db, lds0, nchunks > 1 ? 1 : 0, q, wave_u, lane);
+  }
+  constexpr int kDmaStep = 2 * kDmaLoads + (F == Fmt::kMxFp4 ? 16 : 0);  // codes + a chunk per wave
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(kDmaStep));
   __syncthreads();
 
   Frags<F> f0, f1;
@@ -344,54 +477,68 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(BlockGemmParams
     read_frags<F, 0>(f0, lds, o, 0);
     if constexpr (F == Fmt::kMxFp4) read_scales<false>(sa, sb, lds, o, 0);
   }
-  // a step in stage kSt (compile-time, so LDS addresses fold into the
-  // instructions' offsets). Sub-step s computes from f[s % 2] while the
-  // fragments of sub-step s + 1 load into the other buffer.
-  auto hand_back = [&](auto st_c, int step) {
-    // the last sub-step: the step's stage has been read (each wave's reads
-    // complete before the barrier), every wave's loads of step + 1 have
-    // landed after it, and the stage takes step + 2
-    // (unconditional reads and barrier: after the last full step they read
-    // a stage that is not used, which keeps the registers' flow the same on
-    // every step)
-    // The load is unconditional too: past the last step it loads the last
-    // step again into the stage just read, which nothing reads afterwards
-    // (a conditional load here let the compiler move the MFMAs out of
-    // place).
-    constexpr int st = decltype(st_c)::value;
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    const int ld = step + 2 < nsteps ? step + 2 : nsteps - 1;
-    dma_both<F>(da, db, lds0, ld, ld == nfull, wave_u, lane);
-    read_frags<F, 0>(f0, lds, o, st ^ 1);
-    if constexpr (F == Fmt::kMxFp4) read_scales<false>(sa_n, sb_n, lds, o, st ^ 1);
+  // The loads of step t (parts 0 and 1, see dma_code); a target past the
+  // last step loads the last step again, into a stage that holds the same
+  // bytes or is not read again (so the loop has no branch). Scale chunk c
+  // loads quarter (t + 3) % 4 with step t, t = 4 c - 3 .. 4 c: after the
+  // last reads of chunk c - 2 (the same buffer) and before step 4 c's
+  // scales are read; chunks 0 and 1 are the prologue's.
+  auto dma_part = [&](auto part_c, auto item_c, int t) {
+    constexpr int part = decltype(part_c)::value, item = decltype(item_c)::value;
+    const int tl = t < nsteps ? t : nsteps - 1;
+    const bool half = tl == nfull;
+    if constexpr (item < 8) {
+      // codes: A (item < 4) or B loads 4 part + item % 4
+      const Dma& d = item < 4 ? da : db;
+      dma_code<F>(d, lds0 + (item < 4 ? L::kA : L::kB), tl, half, 4 * part + (item & 3), wave_u, lane);
+    } else if constexpr (F == Fmt::kMxFp4) {
+      const int c = (t + 3) >> 2;
+      const int cl = c < 1 ? 1 : (c > nchunks - 1 ? nchunks - 1 : c);
+      dma_scale(part == 0 ? da : db, lds0 + (part == 0 ? L::kSa : L::kSb), cl, (t + 3) & 3, item - 8, wave_u,
+                lane);
+    }
   };
+  constexpr int kPart = F == Fmt::kMxFp4 ? 10 : 8;  // loads per part
+  // A step in stage st (compile-time, so LDS addresses fold into the
+  // instructions' offsets). Sub-step s computes from f[s % 2] while the
+  // fragments of sub-step s + 1 load into the other buffer; part 1 of step
+  // s + 1's loads goes with sub-step 0, and after the barrier that hands the
+  // stage back, part 0 of step s + 2's with the last sub-step.
   auto do_step = [&](auto st_c, int step) {
     constexpr int st = decltype(st_c)::value;
-    // scheduling fences between sub-steps keep each sub-step's fragment
-    // reads from being hoisted further ahead (which would need more
-    // registers than the two fragment buffers)
+    auto reads = [&](auto ss_c, Frags<F>& f) {
+      return [&, ss_c](auto a_c) {
+        constexpr int a = decltype(a_c)::value;
+        read_frag<F, decltype(ss_c)::value, a>(f, lds, o, st);
+      };
+    };
+    substep<F, 0, 8 + kPart>(acc, f0, sa, sb, [&](auto a_c) {
+      constexpr int a = decltype(a_c)::value;
+      if constexpr (a < 8) {
+        read_frag<F, 1, a>(f1, lds, o, st);
+      } else {
+        dma_part(IC<1>{}, IC<a - 8>{}, step + 1);
+      }
+    });
     if constexpr (kSub == 4) {
-      read_frags<F, 1>(f1, lds, o, st);
-      mfma_substep<F, 0>(acc, f0, sa, sb);
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags<F, 2>(f0, lds, o, st);
-      mfma_substep<F, 1>(acc, f1, sa, sb);
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags<F, 3>(f1, lds, o, st);
-      mfma_substep<F, 2>(acc, f0, sa, sb);
-      __builtin_amdgcn_sched_barrier(0);
-      hand_back(st_c, step);
-      mfma_substep<F, 3>(acc, f1, sa, sb);
-      __builtin_amdgcn_sched_barrier(0);
-    } else {
-      read_frags<F, 1>(f1, lds, o, st);
-      mfma_substep<F, 0>(acc, f0, sa, sb);
-      __builtin_amdgcn_sched_barrier(0);
-      hand_back(st_c, step);
-      mfma_substep<F, 1>(acc, f1, sa, sb);
-      __builtin_amdgcn_sched_barrier(0);
+      substep<F, 1, 8>(acc, f1, sa, sb, reads(IC<2>{}, f0));
+      substep<F, 2, 8>(acc, f0, sa, sb, reads(IC<3>{}, f1));
     }
+    // every wave's reads of this stage are complete and its loads of step
+    // + 1 have landed
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    constexpr int kScaleReads = F == Fmt::kMxFp4 ? 8 : 0;
+    substep<F, kSub - 1, 8 + kScaleReads + kPart>(acc, f1, sa, sb, [&](auto a_c) {
+      constexpr int a = decltype(a_c)::value;
+      if constexpr (a < 8) {
+        read_frag<F, 0, a>(f0, lds, o, st ^ 1);
+      } else if constexpr (a < 8 + kScaleReads) {
+        read_scale_word(sa_n, sb_n, lds, o, step + 1, IC<a - 8>{});
+      } else {
+        dma_part(IC<0>{}, IC<a - 8 - kScaleReads>{}, step + 2);
+      }
+    });
     if constexpr (F == Fmt::kMxFp4) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -413,7 +560,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(BlockGemmParams
     Frags<F> g0, g1;
     read_frags<F, 0>(g0, lds, oh, st);
     if constexpr (F == Fmt::kMxFp4) {
-      read_scales<true>(sa, sb, lds, oh, st);
+      read_scales<true>(sa, sb, lds, oh, nfull);
       read_frags<F, 1>(g1, lds, oh, st);
       mfma_substep<F, 0>(acc, g0, sa, sb);
       mfma_substep<F, 1>(acc, g1, sa, sb);

@@ -317,7 +317,8 @@ int mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t c
  * B [N][K] in MXFP4 (codes qa/qb, scales sa/sb as mxfp4_quantize writes
  * them), float32 accumulation on gfx950's block-scaled FP4 MFMA, C in
  * c_dtype with leading dimension ldc >= N (element alignment suffices).
- * K % 128 == 0 (K == 0 writes zeros); operand pointers 16-byte aligned.
+ * K % 128 == 0 (K == 0 writes zeros), M and N <= 2^30; operand pointers
+ * 16-byte aligned.
  */
 int mxfp4_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
                int64_t M, int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc,
@@ -365,7 +366,8 @@ int fp8_dequantize(const uint8_t* q, const float* tensor_scale, int64_t rows, in
  * float32 accumulation on gfx950's FP8 MFMA (products exact), the scales
  * applied once in the epilogue; C in c_dtype with leading dimension
  * ldc >= N (element alignment suffices). ta / tb: device float32 decode
- * scales as fp8_quantize writes them. K % 64 == 0 (K == 0 writes zeros).
+ * scales as fp8_quantize writes them. K % 64 == 0 (K == 0 writes zeros),
+ * M and N <= 2^30.
  */
 int fp8_gemm(const uint8_t* qa, const float* ta, const uint8_t* qb, const float* tb, int64_t M,
              int64_t N, int64_t K, void* c, int c_dtype, int64_t ldc, hipStream_t stream);
