@@ -423,7 +423,9 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(BlockGemmParams
   using T = Traits<F>;
   using L = Lds<F>;
   constexpr int kSub = T::kSub;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[L::kBytes];
+  // the stages, and after the K loop the epilogue's staging of C
+  constexpr int kLdsBytes = L::kBytes > 4 * kEpilogueWaveBytes ? L::kBytes : 4 * kEpilogueWaveBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -570,7 +572,19 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(BlockGemmParams
   }
   float alpha = 1.0f;
   if constexpr (F == Fmt::kFp8) alpha = __fmul_rn(*p.ta, *p.tb);
-  store_tile<4, kBf16Out>(acc, alpha, p.c, p.ldc, p.M, p.N, m0 + wm * kWave, n0 + wn * kWave, lane);
+  const int64_t r0 = m0 + wm * kWave, c0 = n0 + wn * kWave;
+  constexpr int kElem = kBf16Out ? 2 : 4;
+  const bool lines = r0 + kWave <= p.M && c0 + kWave <= p.N && ((p.ldc * kElem) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(p.c) & 15) == 0;
+  // the loop's last (repeated) loads have landed and every wave is done
+  // with the stages, which the epilogue reuses
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (lines) {
+    store_tile_lds<kBf16Out>(acc, alpha, p.c, p.ldc, r0, c0, lane, lds + wave * kEpilogueWaveBytes);
+  } else {
+    store_tile<4, kBf16Out>(acc, alpha, p.c, p.ldc, p.M, p.N, r0, c0, lane);
+  }
 }
 
 template <Fmt F>

@@ -111,6 +111,68 @@ __device__ __forceinline__ void store_tile(const floatx16_t (&acc)[kT][kT], floa
   }
 }
 
+// LDS bytes store_tile_lds needs per wave (bf16 C: 128 rows of 272 bytes;
+// float32 C: 64 rows of 528 bytes, two passes).
+constexpr int kEpilogueRowBf16 = 128 * 2 + 16;
+constexpr int kEpilogueRowF32 = 128 * 4 + 16;
+constexpr int kEpilogueWaveBytes = 128 * kEpilogueRowBf16;  // >= 64 * kEpilogueRowF32
+static_assert(64 * kEpilogueRowF32 <= kEpilogueWaveBytes, "float32 pass fits the bf16 region");
+
+// Epilogue of a wave's 128 x 128 accumulator tile (kT = 4) staged through
+// LDS: the wave writes its C values (times scale) row-major into its own
+// LDS region (rows padded by 16 bytes), then stores whole rows with 16-byte
+// stores, so each store instruction writes complete 128-byte lines (8 of
+// them) instead of 16-byte pieces of 32 rows. `region` is the wave's LDS
+// region (kEpilogueWaveBytes, 16-byte aligned); the caller has finished all
+// other use of it (a barrier after the last read and load). Only for a tile
+// inside M x N with 16-byte aligned rows of C; others use store_tile.
+template <bool kBf16Out>
+__device__ __forceinline__ void store_tile_lds(const floatx16_t (&acc)[4][4], float scale, void* c, int64_t ldc,
+                                               int64_t row0, int64_t col0, int lane, uint8_t* region) {
+  const int row_l = lane & 31;
+  const int col_l = (lane >> 5) * 4;
+  constexpr int kPasses = kBf16Out ? 1 : 2;      // float32: row blocks 0-1, then 2-3
+  constexpr int kRow = kBf16Out ? kEpilogueRowBf16 : kEpilogueRowF32;
+  constexpr int kElem = kBf16Out ? 2 : 4;
+  constexpr int kRowsPass = 128 / kPasses;
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+#pragma unroll
+    for (int ii = 0; ii < 4 / kPasses; ++ii) {
+      const int i = pass * (4 / kPasses) + ii;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __fmul_rn(acc[i][j][4 * g + e], scale);
+          uint8_t* dst = region + (ii * 32 + row_l) * kRow + (j * 32 + 8 * g + col_l) * kElem;
+          if constexpr (kBf16Out) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]));
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        }
+    }
+    // the wave's own LDS writes are complete before it reads them back
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    constexpr int kChunks = 128 * kElem / 16;  // 16-byte chunks per row
+    constexpr int kRowsPerStore = 64 / kChunks;
+#pragma unroll
+    for (int q = 0; q < kRowsPass / kRowsPerStore; ++q) {
+      const int r = q * kRowsPerStore + lane / kChunks, ch = lane % kChunks;
+      const uint4 v = *reinterpret_cast<const uint4*>(region + r * kRow + 16 * ch);
+      uint8_t* out = static_cast<uint8_t*>(c) + ((row0 + pass * kRowsPass + r) * ldc + col0) * kElem + 16 * ch;
+      *reinterpret_cast<uint4*>(out) = v;
+    }
+    if constexpr (kPasses > 1) {
+      // the next pass overwrites the region: this pass's reads are done
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+    }
+  }
+}
+
 // Writes zeros to C (the K == 0 product).
 __global__ void zero_output_kernel(void* c, int64_t M, int64_t N, int64_t ldc, bool bf16);
 
