@@ -69,11 +69,11 @@ COUNTERS_SUMMARY = "linear_layer_counters.md"
 # quantize kernel; a GEMM call launches 256 x 256 tiles and, for a last
 # partial round, 128 x 128 ones.
 CALL_KERNELS = {
-    "quantize_x_row_rht": (("rht_amax_mfma_kernel<true,", 0),
+    "quantize_x_row_rht": (("rht_amax_mfma_kernel<true>", 0),
                            ("rht_quantize_mfma_kernel<true, false,", 0)),
-    "quantize_w_16x16": (("amax_flat_kernel<unsigned short,", 0),
+    "quantize_w_16x16": (("amax_flat_kernel<unsigned short>", 0),
                          ("quantize_kernel<unsigned short, 1, false>", 0)),
-    "rht_quantize_dy_sr": (("rht_amax_mfma_kernel<false,", 0),
+    "rht_quantize_dy_sr": (("rht_amax_mfma_kernel<false>", 0),
                            ("rht_quantize_mfma_kernel<false, true,", 0)),
     "gemm_fprop": (("gemm_kernel<4, false, true,", 0), ("gemm_kernel<2, false, true,", 0)),
     "gemm_wgrad": (("gemm_kernel<4, false, false,", 0), ("gemm_kernel<2, false, false,", 0)),

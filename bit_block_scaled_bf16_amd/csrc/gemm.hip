@@ -319,7 +319,11 @@ __device__ __forceinline__ void expand_substep(half8_t (&af)[kT], half8_t (&bf)[
 template <int kT, bool kA2D, bool kB2D, bool kAligned, bool kBf16Out>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   using G = Geo<kT>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * G::kStageBytes];
+  // the ring, and after the K loop (kT = 4) the epilogue's staging of C
+  constexpr int kLdsBytes = (kT == 4 && 4 * kEpilogueWaveBytes > kStages * G::kStageBytes)
+                                ? 4 * kEpilogueWaveBytes
+                                : kStages * G::kStageBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -477,9 +481,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     cur = nxt;
   }
 
-  // Epilogue: C = acc * (S_A * S_B).
-  store_tile<kT, kBf16Out>(acc, __fmul_rn(*p.ta, *p.tb), p.c, p.ldc, p.M, p.N, m0 + wm * G::kWave,
-                           n0 + wn * G::kWave, lane);
+  // Epilogue: C = acc * (S_A * S_B). Whole lines through LDS for a 128 x 128
+  // wave tile inside C with aligned rows (the loop's last barrier follows
+  // its last LDS read and load).
+  const float alpha = __fmul_rn(*p.ta, *p.tb);
+  const int64_t r0 = m0 + wm * G::kWave, c0 = n0 + wn * G::kWave;
+  if constexpr (kT == 4) {
+    constexpr int kElem = kBf16Out ? 2 : 4;
+    const bool lines = r0 + G::kWave <= p.M && c0 + G::kWave <= p.N && ((p.ldc * kElem) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(p.c) & 15) == 0;
+    if (lines) {
+      store_tile_lds<kBf16Out>(acc, alpha, p.c, p.ldc, r0, c0, lane, lds + wave * kEpilogueWaveBytes);
+      return;
+    }
+  }
+  store_tile<kT, kBf16Out>(acc, alpha, p.c, p.ldc, p.M, p.N, r0, c0, lane);
 }
 
 }  // namespace

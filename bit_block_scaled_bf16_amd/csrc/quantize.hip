@@ -47,7 +47,6 @@ __device__ __forceinline__ int staged_code_offset(int col, int byte) {
   return col * kLdsCodeStride + ((((byte >> 4) ^ ((col >> 3) & 7)) << 4) | (byte & 15));
 }
 constexpr int64_t kMaxTileBlocks = 1024;  // workgroups of the tile-shaped amax kernels
-constexpr int64_t kInfinityCacheBytes = int64_t(256) << 20;  // MI355X's memory-side cache
 
 // kModeRowRHT: the 1x16 row copy (round to nearest) and the Hadamard column
 // copy of the same tensor, each with its own tensor scale, from one read.
@@ -198,26 +197,12 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// An ordinary (cache-allocating) 16-byte load: the amax pass uses it when
-// the quantize pass that follows can find the input still in the Infinity
-// Cache.
-__device__ __forceinline__ uint4 load_keep(const void* p) { return *static_cast<const uint4*>(p); }
-
-template <bool kKeep>
-__device__ __forceinline__ uint4 load_amax(const void* p) {
-  if constexpr (kKeep) {
-    return load_keep(p);
-  } else {
-    return load_stream(p);
-  }
-}
-
 __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, a),
                                                                 __builtin_bit_cast(ushort2_t, b)));
 }
 
-template <typename InT, bool kKeep>
+template <typename InT>
 __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* __restrict__ x, int64_t n,
                                                              uint32_t* __restrict__ partials) {
   __shared__ uint32_t lds4[kThreads / 64];
@@ -232,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* __restri
 #pragma unroll
     for (int u = 0; u < kFlatUnroll; ++u) {
       const int64_t i = base + u * kThreads;
-      r[u] = i < nvec ? load_amax<kKeep>(xv + i) : make_uint4(0u, 0u, 0u, 0u);
+      r[u] = i < nvec ? load_stream(xv + i) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < kFlatUnroll; ++u) {
@@ -1025,17 +1010,16 @@ __device__ __forceinline__ AmaxUnit locate_amax_unit(int64_t u, int64_t rows, in
 
 // raw[4 (2 s + hc) + i] = token r0 + 16 s + i, columns c0 + 128 hc .. + 7;
 // parts past the matrix read its first 8 values (never used).
-template <bool kKeep>
 __device__ __forceinline__ void load_amax_part(const uint16_t* __restrict__ x, int64_t ldx,
                                                const AmaxUnit& a, int s, int hc, uint4 (&raw)[16]) {
   const bool ok = (hc == 0 ? a.valid0 : a.valid1) && s < a.steps;
   const uint16_t* base = x + (ok ? (a.r0 + 16 * s) * ldx + a.c0 + 128 * hc : 0);
   const int64_t stride = ok ? ldx : 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) raw[4 * (2 * s + hc) + i] = load_amax<kKeep>(base + i * stride);
+  for (int i = 0; i < 4; ++i) raw[4 * (2 * s + hc) + i] = load_stream(base + i * stride);
 }
 
-template <bool kDual, bool kKeep>
+template <bool kDual>
 __global__ __launch_bounds__(kThreads) void rht_amax_mfma_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, uint32_t sign_mask,
     int64_t units, uint32_t* __restrict__ partials, uint32_t* __restrict__ partials_plain) {
@@ -1050,7 +1034,7 @@ __global__ __launch_bounds__(kThreads) void rht_amax_mfma_kernel(
   AmaxUnit cu = locate_amax_unit(u, rows, cols);
   uint4 raw[16];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) load_amax_part<kKeep>(x, ldx, cu, q >> 1, q & 1, raw);
+  for (int q = 0; q < 4; ++q) load_amax_part(x, ldx, cu, q >> 1, q & 1, raw);
   for (; u < units; u += wave_stride) {
     const AmaxUnit uc = cu;
     const bool has_next = u + wave_stride < units;
@@ -1095,7 +1079,7 @@ __global__ __launch_bounds__(kThreads) void rht_amax_mfma_kernel(
         }
         if (hc) { mt1 = mt; mp1 = mp; } else { mt0 = mt; mp0 = mp; }
       }
-      if (has_next) load_amax_part<kKeep>(x, ldx, cu, s, hc, raw);
+      if (has_next) load_amax_part(x, ldx, cu, s, hc, raw);
     }
     // parts whose columns are past the matrix transformed placeholder data
     if (uc.valid0) {
@@ -1560,17 +1544,12 @@ int64_t amax_workgroups(int64_t rows, int64_t cols, int64_t ldx, bool rht, int64
 
 template <typename InT>
 int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
-                uint32_t sign_mask, float* amax_ws, hipStream_t stream, bool dual = false,
-                bool keep = false) {
+                uint32_t sign_mask, float* amax_ws, hipStream_t stream, bool dual = false) {
   uint32_t* partials = reinterpret_cast<uint32_t*>(amax_ws) + kPartialsOffset;
   uint32_t* partials_plain = partials + kMaxPartials;
   const int64_t g = amax_workgroups(rows, cols, ldx, rht, sizeof(InT));
   if (!rht && ldx == cols) {
-    if (keep) {
-      amax_flat_kernel<InT, true><<<static_cast<unsigned>(g), kThreads, 0, stream>>>(x, rows * cols, partials);
-    } else {
-      amax_flat_kernel<InT, false><<<static_cast<unsigned>(g), kThreads, 0, stream>>>(x, rows * cols, partials);
-    }
+    amax_flat_kernel<InT><<<static_cast<unsigned>(g), kThreads, 0, stream>>>(x, rows * cols, partials);
   } else {
     const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
     const unsigned gg = static_cast<unsigned>(g);
@@ -1579,18 +1558,12 @@ int launch_amax(const InT* x, int64_t rows, int64_t cols, int64_t ldx, bool rht,
       const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
       const int64_t units = ((rows + kAmaxUnitRows - 1) / kAmaxUnitRows) *
                             ((cols + kAmaxUnitCols - 1) / kAmaxUnitCols);
-      if (dual && keep) {
-        rht_amax_mfma_kernel<true, true><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask, units,
-                                                                      partials, partials_plain);
-      } else if (dual) {
-        rht_amax_mfma_kernel<true, false><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask, units,
-                                                                       partials, partials_plain);
-      } else if (keep) {
-        rht_amax_mfma_kernel<false, true><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask,
-                                                                       units, partials, nullptr);
+      if (dual) {
+        rht_amax_mfma_kernel<true><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask, units,
+                                                                partials, partials_plain);
       } else {
-        rht_amax_mfma_kernel<false, false><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask,
-                                                                        units, partials, nullptr);
+        rht_amax_mfma_kernel<false><<<gg, kThreads, 0, stream>>>(xb, rows, cols, ldx, sign_mask, units,
+                                                                 partials, nullptr);
       }
     } else if (rht && dual) {
       amax_tile_kernel<InT, true, false, true><<<gg, kThreads, 0, stream>>>(
@@ -1718,20 +1691,10 @@ int launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
   p.amax_out_t = nullptr;
   p.tensor_scale_t = q.tensor_scale_t;
   if (q.amax_in == nullptr) {
-    // Infinity Cache residency: when the input and what the quantize pass
-    // writes (codes and 1D scales, 9/16 byte per element and copy) fit in
-    // the 256 MiB cache together, the amax pass reads with allocating loads
-    // and the quantize pass finds the input there; otherwise both passes
-    // stream with nontemporal loads (measured: a 168 MB activation's
-    // one-call pair gains about 4 us, a 210 MB weight's 16x16 pair loses
-    // about 8 us with allocating loads)
-    const int64_t elems = q.rows * q.cols;
-    const int64_t copies = dual ? 2 : (q.rht ? 1 : ((q.outputs & 1) != 0) + ((q.outputs & 2) != 0));
-    const bool keep = elems * (bf16 ? 2 : 4) + copies * (elems / 2 + elems / 16) <= kInfinityCacheBytes;
     const int n = bf16 ? launch_amax(static_cast<const uint16_t*>(q.x), q.rows, q.cols, q.ldx,
-                                     q.rht, q.sign_mask, q.amax_ws, stream, dual, keep)
+                                     q.rht, q.sign_mask, q.amax_ws, stream, dual)
                        : launch_amax(static_cast<const float*>(q.x), q.rows, q.cols, q.ldx,
-                                     q.rht, q.sign_mask, q.amax_ws, stream, dual, keep);
+                                     q.rht, q.sign_mask, q.amax_ws, stream, dual);
     if (n < 0) return -1;
     const uint32_t* base = reinterpret_cast<const uint32_t*>(q.amax_ws) + kPartialsOffset;
     p.n_partials = n;
