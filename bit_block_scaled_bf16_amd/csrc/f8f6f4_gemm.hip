@@ -503,9 +503,10 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(BlockGemmParams
   constexpr int kPart = F == Fmt::kMxFp4 ? 10 : 8;  // loads per part
   // A step in stage st (compile-time, so LDS addresses fold into the
   // instructions' offsets). Sub-step s computes from f[s % 2] while the
-  // fragments of sub-step s + 1 load into the other buffer; part 1 of step
-  // s + 1's loads goes with sub-step 0, and after the barrier that hands the
-  // stage back, part 0 of step s + 2's with the last sub-step.
+  // fragments of sub-step s + 1 load into the other buffer; after the
+  // barrier that hands the stage back, the last sub-step issues part 0 of
+  // step s + 2's loads (FP8: both parts), and FP4's part 1 follows with the
+  // next step's sub-steps 0 and 1.
   auto do_step = [&](auto st_c, int step) {
     constexpr int st = decltype(st_c)::value;
     auto reads = [&](auto ss_c, Frags<F>& f) {
@@ -514,7 +515,13 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(BlockGemmParams
         read_frag<F, decltype(ss_c)::value, a>(f, lds, o, st);
       };
     };
-    substep<F, 0, 8 + kPart>(acc, f0, sa, sb, [&](auto a_c) {
+    // Part 1 of step s + 1's loads: FP4 (16 MFMAs of 32 cycles per
+    // sub-step) spreads it over sub-steps 0 and 1; FP8 (64-cycle MFMAs)
+    // issued it with part 0 after the previous barrier (each measured faster
+    // than the other placement).
+    constexpr int kP0 = kSub == 4 ? kPart / 2 : 0;  // part 1 loads in sub-step 0
+    constexpr int kP1 = kSub == 4 ? kPart - kP0 : 0;  // ... and in sub-step 1
+    substep<F, 0, 8 + kP0>(acc, f0, sa, sb, [&](auto a_c) {
       constexpr int a = decltype(a_c)::value;
       if constexpr (a < 8) {
         read_frag<F, 1, a>(f1, lds, o, st);
@@ -523,7 +530,14 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(BlockGemmParams
       }
     });
     if constexpr (kSub == 4) {
-      substep<F, 1, 8>(acc, f1, sa, sb, reads(IC<2>{}, f0));
+      substep<F, 1, 8 + kP1>(acc, f1, sa, sb, [&](auto a_c) {
+        constexpr int a = decltype(a_c)::value;
+        if constexpr (a < 8) {
+          read_frag<F, 2, a>(f0, lds, o, st);
+        } else {
+          dma_part(IC<1>{}, IC<a - 8 + kP0>{}, step + 1);
+        }
+      });
       substep<F, 2, 8>(acc, f0, sa, sb, reads(IC<3>{}, f1));
     }
     // every wave's reads of this stage are complete and its loads of step
@@ -531,14 +545,17 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(BlockGemmParams
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     constexpr int kScaleReads = F == Fmt::kMxFp4 ? 8 : 0;
-    substep<F, kSub - 1, 8 + kScaleReads + kPart>(acc, f1, sa, sb, [&](auto a_c) {
+    constexpr int kLast = kSub == 4 ? kPart : 2 * kPart;  // loads after the barrier
+    substep<F, kSub - 1, 8 + kScaleReads + kLast>(acc, f1, sa, sb, [&](auto a_c) {
       constexpr int a = decltype(a_c)::value;
       if constexpr (a < 8) {
         read_frag<F, 0, a>(f0, lds, o, st ^ 1);
       } else if constexpr (a < 8 + kScaleReads) {
         read_scale_word(sa_n, sb_n, lds, o, step + 1, IC<a - 8>{});
-      } else {
+      } else if constexpr (a < 8 + kScaleReads + kPart) {
         dma_part(IC<0>{}, IC<a - 8 - kScaleReads>{}, step + 2);
+      } else {
+        dma_part(IC<1>{}, IC<a - 8 - kScaleReads - kPart>{}, step + 2);
       }
     });
     if constexpr (F == Fmt::kMxFp4) {
