@@ -29,14 +29,17 @@ the FETCH_SIZE / WRITE_SIZE counters) and `counters` (VALU / MFMA busy)
 come from the committed summaries in profiles/ and are null once the kernel
 source has changed since they were taken. They are regenerated with:
 
+  NEXT=mx_quantize_x,mx_quantize_w,mx_gemm_fprop,fp8_quantize_x,fp8_quantize_w,\
+fp8_quantize_dy,fp8_gemm_fprop,fp8_gemm_wgrad
   rocprofv3 --kernel-trace --stats -d <d> -o run --output-format csv -- \
-      python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-next
+      python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --next-only $NEXT
   rocprofv3 --pmc FETCH_SIZE -d <d1> -o run --output-format csv -- \
-      python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-next --copy-calibration-mib 1024
+      python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --next-only $NEXT \
+      --copy-calibration-mib 1024
   rocprofv3 --pmc WRITE_SIZE -d <d2> ... (same command)
   rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_WAVES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU \
       SQ_INSTS_VALU SQ_INSTS_MFMA -d <d3> -o run --output-format csv -- \
-      python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-next
+      python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --next-only $NEXT
   python -m bit_block_scaled_bf16_amd.profiling stats|traffic|counters ...
 """
 
@@ -65,7 +68,7 @@ TOKENS, HIDDEN, FFN = 16384, 5120, 20480
 TRAFFIC_SUMMARY = "linear_layer_traffic.md"
 COUNTERS_SUMMARY = "linear_layer_counters.md"
 # Kernels of each call, as (short-name fragment, dispatch index) in a
-# profiled `--steps 1 --no-next` run: a quantize call is an amax kernel and a
+# profiled `--steps 1` run: a quantize call is an amax kernel and a
 # quantize kernel; a GEMM call launches 256 x 256 tiles and, for a last
 # partial round, 128 x 128 ones.
 CALL_KERNELS = {
@@ -80,6 +83,18 @@ CALL_KERNELS = {
 }
 CALL_SOURCE = {n: ("gemm_kernel" if n.startswith("gemm") else "quantize_kernel")
                for n in CALL_KERNELS}
+# The same for calls after the step, in a profiled run with `--next-only`
+# naming them: each runs once untimed, then once per timed round, in the
+# order next_calls() lists them (so the two FP8 GEMMs alternate).
+NEXT_KERNELS = {
+    "mx_quantize_x": (("mx_quantize_kernel<unsigned short>", 2),),
+    "mx_quantize_w": (("mx_quantize_kernel<unsigned short>", 3),),
+    "mx_gemm_fprop": (("block_gemm_kernel<(Fmt)0", 1),),
+    "fp8_gemm_fprop": (("block_gemm_kernel<(Fmt)1", 2),),
+    "fp8_gemm_wgrad": (("block_gemm_kernel<(Fmt)1", 3),),
+}
+NEXT_SOURCE = {n: ("mxfp4" if n.startswith("mx_quantize") else "block_gemm_kernel")
+               for n in NEXT_KERNELS}
 
 
 def parse():
@@ -90,6 +105,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true",
                     help="time only the step (profiling runs: the later calls share its kernels)")
+    ap.add_argument("--next-only", default="",
+                    help="comma-separated names of calls after the step: time only these, "
+                         "and none of the later blocks (profiling runs of those kernels)")
     ap.add_argument("--tokens", type=int, default=TOKENS)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one copy-like kernel (torch.bitwise_not on int32) "
@@ -604,6 +622,12 @@ def main():
     if not args.no_next:
         reps = max(args.steps, 5)
         nxt = step.next_calls()
+        only = [n for n in args.next_only.split(",") if n]
+        if only:
+            unknown = set(only) - {n for n, _ in nxt}
+            if unknown:
+                sys.exit(f"--next-only: unknown calls {sorted(unknown)}")
+            nxt = [c for c in nxt if c[0] in only]
         us = time_calls(torch, nxt, reps, rotate=step.advance)
         rows = {}
         for name, _ in nxt:
@@ -611,8 +635,16 @@ def main():
             peak = (FP4_MFMA_PEAK_TFLOPS if unit.startswith("FP4") else
                     FP8_MFMA_PEAK_TFLOPS if unit.startswith("FP8") else
                     HBM_PEAK_GBS if unit == "GB/s" else MFMA_PEAK_TFLOPS)
-            rows[name] = rate_row(us[name], amount, unit, peak)
+            traffic = (profiling.kernel_traffic(traffic_md, NEXT_KERNELS[name], NEXT_SOURCE[name])
+                       if name in NEXT_KERNELS else None)
+            rows[name] = rate_row(us[name], amount, unit, peak, traffic)
+            if name in NEXT_KERNELS:
+                rows[name]["counters"] = profiling.kernel_counters(
+                    counters_md, NEXT_KERNELS[name], NEXT_SOURCE[name])
         assert int(step.status.cpu()[0]) == 0, "non-finite amax"
+    if not args.no_next and only:
+        next_block = {"selected": rows}
+    elif not args.no_next:
         next_block = {
             "dgrad": {k: rows[k] for k in ("quantize_dy_1x16_sr", "gemm_dgrad")},
             "variants": {k: rows[k] for k in ("quantize_x_1x16", "rht_quantize_x_rn",
