@@ -58,6 +58,20 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// Stores of C. C is written once and not read back by the kernel, so its
+// stores are nontemporal: they do not displace the operand panels that other
+// workgroups of the same XCD still read from L2.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_c8(void* dst, uint32_t lo, uint32_t hi) {
+  const u32x2_t v = {lo, hi};
+  __builtin_nontemporal_store(v, static_cast<u32x2_t*>(dst));
+}
+__device__ __forceinline__ void store_c16(void* dst, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4_t v = {a, b, c, d};
+  __builtin_nontemporal_store(v, static_cast<u32x4_t*>(dst));
+}
+
 // Epilogue of a wave's kT x kT accumulator tiles: C = acc * scale. The MFMAs
 // took B as their first operand, so each accumulator tile is C^T in the MFMA
 // output layout: lane l holds row l % 32 of the 32 x 32 tile and, in elements
@@ -86,12 +100,11 @@ __device__ __forceinline__ void store_tile(const floatx16_t (&acc)[kT][kT], floa
         for (int e = 0; e < 4; ++e) v[e] = __fmul_rn(acc[i][j][4 * g + e], scale);
         if (vec_ok && col + 3 < N) {
           if constexpr (kBf16Out) {
-            const uint32_t lo = f32x2_to_bf16x2(v[0], v[1]);
-            const uint32_t hi = f32x2_to_bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(c) + row * ldc + col) = make_uint2(lo, hi);
+            store_c8(static_cast<uint16_t*>(c) + row * ldc + col, f32x2_to_bf16x2(v[0], v[1]),
+                     f32x2_to_bf16x2(v[2], v[3]));
           } else {
-            *reinterpret_cast<float4*>(static_cast<float*>(c) + row * ldc + col) =
-                make_float4(v[0], v[1], v[2], v[3]);
+            store_c16(static_cast<float*>(c) + row * ldc + col, __float_as_uint(v[0]),
+                      __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
           }
         } else {
 #pragma unroll
@@ -121,8 +134,8 @@ static_assert(64 * kEpilogueRowF32 <= kEpilogueWaveBytes, "float32 pass fits the
 // Epilogue of a wave's 128 x 128 accumulator tile (kT = 4) staged through
 // LDS: the wave writes its C values (times scale) row-major into its own
 // LDS region (rows padded by 16 bytes), then stores whole rows with 16-byte
-// stores, so each store instruction writes complete 128-byte lines (8 of
-// them) instead of 16-byte pieces of 32 rows. `region` is the wave's LDS
+// nontemporal stores, so each store instruction writes complete 128-byte
+// lines (8 of them) instead of 16-byte pieces of 32 rows. `region` is the wave's LDS
 // region (kEpilogueWaveBytes, 16-byte aligned); the caller has finished all
 // other use of it (a barrier after the last read and load). Only for a tile
 // inside M x N with 16-byte aligned rows of C; others use store_tile.
@@ -164,7 +177,7 @@ __device__ __forceinline__ void store_tile_lds(const floatx16_t (&acc)[4][4], fl
       const int r = q * kRowsPerStore + lane / kChunks, ch = lane % kChunks;
       const uint4 v = *reinterpret_cast<const uint4*>(region + r * kRow + 16 * ch);
       uint8_t* out = static_cast<uint8_t*>(c) + ((row0 + pass * kRowsPass + r) * ldc + col0) * kElem + 16 * ch;
-      *reinterpret_cast<uint4*>(out) = v;
+      store_c16(out, v.x, v.y, v.z, v.w);
     }
     if constexpr (kPasses > 1) {
       // the next pass overwrites the region: this pass's reads are done
