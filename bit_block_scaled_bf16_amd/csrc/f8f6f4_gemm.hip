@@ -166,21 +166,36 @@ __device__ __forceinline__ void dma_both(const Dma& da, const Dma& db, uint32_t 
   dma_step<F>(db, lds + L::kB + st * kCodeBytes, step, half, wave, lane);
 }
 
+// Scale words in LDS: a row's 32-byte chunk holds its eight 4-byte words
+// (two per step) with word w at position w ^ scale_swizzle(row), so that the
+// 64 lanes of a scale read (32 rows, two words each) fall in 64 distinct
+// banks instead of eight rows sharing each bank.
+__device__ __forceinline__ int scale_swizzle(int row) { return 2 * ((row >> 3) & 3); }
+static_assert(Traits<Fmt::kMxFp4>::kChunkRow == 32 && Traits<Fmt::kMxFp4>::kScaleRow == 8,
+              "eight 4-byte words per row chunk, two per step: the swizzle stays inside the chunk");
+
+// Load k (k = 2 q + e) of a wave's scale chunk fills rows 64 w + 8 k .. + 7;
+// lane j lands in position j % 8 of row 64 w + 8 k + j / 8 and so fetches
+// word (j % 8) ^ scale_swizzle(8 k) of the chunk. A word past the row's K / 32
+// (the last chunk of a K that is not a multiple of 1024) reads the row's
+// first bytes instead: no step reads it.
+__device__ __forceinline__ int64_t scale_src(const Dma& d, int chunk, int k, int lane) {
+  constexpr int kRow = Traits<Fmt::kMxFp4>::kChunkRow;
+  const int64_t want = static_cast<int64_t>(chunk) * kRow + 4 * ((lane & 7) ^ scale_swizzle(8 * k));
+  return want + 4 <= d.srb ? want : 0;
+}
+
 // Quarter q (loads 2q and 2q + 1, 16 rows of this wave's 64) of scale chunk
-// `chunk` (MXFP4) of one operand into the LDS buffer at byte address buf:
-// lane j of load k carries bytes 4 (j % 8) .. + 3 of the chunk's 32 bytes of
-// row 64 w + 8 k + j / 8. Bytes past the row's K / 32 (the last chunk of a K
-// that is not a multiple of 1024) read the row's first bytes instead.
+// `chunk` (MXFP4) of one operand into the LDS buffer at byte address buf.
 __device__ __forceinline__ void dma_scale_quarter(const Dma& d, uint32_t buf, int chunk, int q, int wave,
                                                   int lane) {
   constexpr int kRow = Traits<Fmt::kMxFp4>::kChunkRow;
-  const int64_t want = static_cast<int64_t>(chunk) * kRow + 4 * (lane & 7);
-  const int64_t off = want + 4 <= d.srb ? want : 0;  // past the row's end: its first bytes
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int r = 16 * q + 8 * e;  // load 2 q + e: rows r .. r + 7 of the wave's 64
     const int row = min(d.row + r, d.last);
-    lds_dma<4>(d.s + static_cast<int64_t>(row) * d.srb + off, buf + (64 * wave + r) * kRow);
+    lds_dma<4>(d.s + static_cast<int64_t>(row) * d.srb + scale_src(d, chunk, 2 * q + e, lane),
+               buf + (64 * wave + r) * kRow);
   }
 }
 
@@ -210,11 +225,10 @@ __device__ __forceinline__ void dma_scale(const Dma& d, uint32_t operand, int ch
                                           int lane) {
   using L = Lds<Fmt::kMxFp4>;
   constexpr int kRow = Traits<Fmt::kMxFp4>::kChunkRow;
-  const int64_t want = static_cast<int64_t>(chunk) * kRow + 4 * (lane & 7);
-  const int64_t off = want + 4 <= d.srb ? want : 0;  // past the row's end: its first bytes
   const int r = 16 * q + 8 * e;
   const int row = min(d.row + r, d.last);
-  lds_dma<4>(d.s + static_cast<int64_t>(row) * d.srb + off, operand + (chunk & 1) * L::kScaleBuf + (64 * wave + r) * kRow);
+  lds_dma<4>(d.s + static_cast<int64_t>(row) * d.srb + scale_src(d, chunk, 2 * q + e, lane),
+             operand + (chunk & 1) * L::kScaleBuf + (64 * wave + r) * kRow);
 }
 
 template <int kN>
@@ -247,6 +261,7 @@ struct Frags {
 struct FragOffsets {
   int a[4], b[4];
   int sa, sb;  // the lane's scale word (full step) or 16-bit half (half step)
+  int sx;      // XOR on a step's byte offset within the row's chunk: 4 scale_swizzle(row)
 };
 
 template <Fmt F>
@@ -264,6 +279,7 @@ __device__ __forceinline__ FragOffsets frag_offsets(int wm, int wn, int lane, bo
   }
   o.sa = L::kSa + ra * Traits<F>::kChunkRow + (half ? 2 * h : 4 * h);
   o.sb = L::kSb + rb * Traits<F>::kChunkRow + (half ? 2 * h : 4 * h);
+  o.sx = 4 * scale_swizzle(rl);  // rows ra and rb (and + 32 i) share it
   return o;
 }
 
@@ -321,7 +337,8 @@ template <bool kHalf>
 __device__ __forceinline__ void read_scales(uint32_t (&sa)[4], uint32_t (&sb)[4], const uint8_t* __restrict__ lds,
                                             const FragOffsets& o, int step) {
   using T = Traits<Fmt::kMxFp4>;
-  const int soff = ((step / T::kChunkSteps) & 1) * Lds<Fmt::kMxFp4>::kScaleBuf + (step % T::kChunkSteps) * T::kScaleRow;
+  const int soff = ((step / T::kChunkSteps) & 1) * Lds<Fmt::kMxFp4>::kScaleBuf +
+                   (((step % T::kChunkSteps) * T::kScaleRow) ^ o.sx);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (kHalf) {
@@ -341,7 +358,8 @@ template <int kN>
 __device__ __forceinline__ void read_scale_word(uint32_t (&sa)[4], uint32_t (&sb)[4], const uint8_t* __restrict__ lds,
                                                 const FragOffsets& o, int step, IC<kN>) {
   using T = Traits<Fmt::kMxFp4>;
-  const int soff = ((step / T::kChunkSteps) & 1) * Lds<Fmt::kMxFp4>::kScaleBuf + (step % T::kChunkSteps) * T::kScaleRow;
+  const int soff = ((step / T::kChunkSteps) & 1) * Lds<Fmt::kMxFp4>::kScaleBuf +
+                   (((step % T::kChunkSteps) * T::kScaleRow) ^ o.sx);
   constexpr int i = kN & 3;
   if constexpr (kN < 4) {
     sa[i] = *reinterpret_cast<const uint32_t*>(lds + o.sa + soff + i * 32 * T::kChunkRow);
@@ -418,6 +436,33 @@ __device__ __forceinline__ void substep(floatx16_t (&acc)[4][4], const Frags<F>&
 // 6 bits, split over bits 3:0 and 15:14), expcnt and lgkmcnt not waited for.
 constexpr int wait_vmcnt(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
 
+
+// Workgroup b -> tile (row-major tile index). Workgroups are handed to the 8
+// XCDs in turn (b % 8), and each XCD has its own L2. When the tile grid
+// divides into 4 x 8 blocks, the 32 workgroups an XCD runs side by side take
+// one such block, so they read 12 operand panels between them (in the
+// row-major order they read about 13 spread over several panel rows and,
+// started at different times, reuse less of them from L2). Blocks are taken
+// 8 at a time, one per XCD, in row-major block order; blocks past the last
+// full set of 8 follow in plain order. A bijection on [0, tiles).
+__device__ __forceinline__ int64_t tile_of(int64_t b, int64_t tiles_m, int64_t tiles_n) {
+  if ((tiles_m & 3) || (tiles_n & 7)) return b;
+  const int64_t blocks_n = tiles_n >> 3;
+  const int64_t blocks = (tiles_m >> 2) * blocks_n;
+  const int64_t full = blocks & ~static_cast<int64_t>(7);
+  int64_t blk, i;
+  if (b < full * 32) {
+    const int64_t l = b >> 3;  // this XCD's l-th workgroup
+    blk = (l >> 5) * 8 + (b & 7);
+    i = l & 31;
+  } else {
+    blk = full + ((b - full * 32) >> 5);
+    i = (b - full * 32) & 31;
+  }
+  const int64_t bm = blk / blocks_n, bn = blk - bm * blocks_n;
+  return (bm * 4 + (i >> 3)) * tiles_n + bn * 8 + (i & 7);
+}
+
 template <Fmt F, bool kBf16Out>
 __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(BlockGemmParams p) {
   using T = Traits<F>;
@@ -430,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(BlockGemmParams
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t tiles_n = (p.N + kTile - 1) / kTile;
-  const int64_t t = blockIdx.x;
+  const int64_t t = tile_of(blockIdx.x, (p.M + kTile - 1) / kTile, tiles_n);
   const int64_t m0 = (t / tiles_n) * kTile, n0 = (t - (t / tiles_n) * tiles_n) * kTile;
   const int64_t K = p.K;
   // K % (kBK / 2) == 0, K > 0: nfull whole steps and possibly a half step

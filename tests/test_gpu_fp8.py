@@ -149,8 +149,11 @@ def test_fp8_empty_and_non_finite():
 
 
 @pytest.mark.parametrize("m,n,k", [(32, 32, 64), (256, 256, 64), (300, 520, 128), (33, 47, 192),
-                                   (512, 768, 1024), (2500, 2608, 512), (272, 256, 5120)])
+                                   (512, 768, 1024), (2500, 2608, 512), (272, 256, 5120),
+                                   (3072, 6144, 128)])
 def test_fp8_gemm_parity(m, n, k):
+    """(3072, 6144, 128): 12 x 24 tiles, nine 4 x 8 tile blocks: eight handed
+    to the XCDs together, one after them in plain order."""
     torch = require_gpu()
     import bit_block_scaled_bf16_amd as nv
 

@@ -54,8 +54,10 @@ def test_mx_quantize_padded_rows_and_extremes():
 
 @pytest.mark.parametrize("m,n,k", [(32, 32, 128), (256, 256, 128), (300, 520, 256),
                                    (512, 768, 1024), (33, 47, 384), (2500, 2608, 512),
-                                   (272, 256, 5120)])
+                                   (272, 256, 5120), (3072, 6144, 256)])
 def test_mx_gemm_parity(m, n, k):
+    """(3072, 6144, 256): 12 x 24 tiles, nine 4 x 8 tile blocks: eight handed
+    to the XCDs together, one after them in plain order."""
     require_gpu()
     import torch
 
