@@ -437,32 +437,6 @@ __device__ __forceinline__ void substep(floatx16_t (&acc)[4][4], const Frags<F>&
 constexpr int wait_vmcnt(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
 
 
-// Workgroup b -> tile (row-major tile index). Workgroups are handed to the 8
-// XCDs in turn (b % 8), and each XCD has its own L2. When the tile grid
-// divides into 4 x 8 blocks, the 32 workgroups an XCD runs side by side take
-// one such block, so they read 12 operand panels between them (in the
-// row-major order they read about 13 spread over several panel rows and,
-// started at different times, reuse less of them from L2). Blocks are taken
-// 8 at a time, one per XCD, in row-major block order; blocks past the last
-// full set of 8 follow in plain order. A bijection on [0, tiles).
-__device__ __forceinline__ int64_t tile_of(int64_t b, int64_t tiles_m, int64_t tiles_n) {
-  if ((tiles_m & 3) || (tiles_n & 7)) return b;
-  const int64_t blocks_n = tiles_n >> 3;
-  const int64_t blocks = (tiles_m >> 2) * blocks_n;
-  const int64_t full = blocks & ~static_cast<int64_t>(7);
-  int64_t blk, i;
-  if (b < full * 32) {
-    const int64_t l = b >> 3;  // this XCD's l-th workgroup
-    blk = (l >> 5) * 8 + (b & 7);
-    i = l & 31;
-  } else {
-    blk = full + ((b - full * 32) >> 5);
-    i = (b - full * 32) & 31;
-  }
-  const int64_t bm = blk / blocks_n, bn = blk - bm * blocks_n;
-  return (bm * 4 + (i >> 3)) * tiles_n + bn * 8 + (i & 7);
-}
-
 template <Fmt F, bool kBf16Out>
 __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(BlockGemmParams p) {
   using T = Traits<F>;

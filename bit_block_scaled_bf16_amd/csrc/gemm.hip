@@ -84,7 +84,7 @@ struct GemmParams {
   const float* tb;
   void* c;
   int64_t M, N, K, ldc;
-  int64_t tile0;  // first 256 x 256 tile (row-major over C) of this launch
+  int64_t tile0;  // tile_of argument of this launch's first tile (see the kernel)
 };
 
 // ---------------------------------------------------------------------------
@@ -312,9 +312,11 @@ __device__ __forceinline__ void expand_substep(half8_t (&af)[kT], half8_t (&bf)[
 }
 
 // ---------------------------------------------------------------------------
-// The kernel. kT = 4: one 256 x 256 tile per workgroup, tile tile0 +
-// blockIdx. kT = 2: one 128 x 128 quarter of 256 x 256 tile
-// tile0 + blockIdx / 4 per workgroup.
+// The kernel. kT = 4: one 256 x 256 tile per workgroup, tile
+// tile_of(tile0 + blockIdx). kT = 2: one 128 x 128 quarter of 256 x 256 tile
+// tile_of(tile0 + blockIdx / 4) per workgroup. The two launches of a call
+// take consecutive ranges of tile_of's argument, so they cover every tile
+// once.
 // ---------------------------------------------------------------------------
 template <int kT, bool kA2D, bool kB2D, bool kAligned, bool kBf16Out>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
@@ -329,14 +331,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t tiles_n = (p.N + kBigTile - 1) / kBigTile;
+  const int64_t tiles_m = (p.M + kBigTile - 1) / kBigTile;
   int64_t m0, n0;
   if constexpr (kT == 4) {
-    const int64_t t = p.tile0 + static_cast<int64_t>(blockIdx.x);
+    const int64_t t = tile_of(p.tile0 + static_cast<int64_t>(blockIdx.x), tiles_m, tiles_n);
     m0 = (t / tiles_n) * kBigTile;
     n0 = (t - (t / tiles_n) * tiles_n) * kBigTile;
   } else {
     static_assert(kT == 2, "tile configurations: 4 x 4 and 2 x 2 MFMA tiles per wave");
-    const int64_t t = p.tile0 + static_cast<int64_t>(blockIdx.x >> 2);
+    const int64_t t = tile_of(p.tile0 + static_cast<int64_t>(blockIdx.x >> 2), tiles_m, tiles_n);
     const int q = blockIdx.x & 3;
     m0 = (t / tiles_n) * kBigTile + G::kTile * (q >> 1);
     n0 = (t - (t / tiles_n) * tiles_n) * kBigTile + G::kTile * (q & 1);

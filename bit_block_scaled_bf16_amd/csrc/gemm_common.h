@@ -186,6 +186,43 @@ __device__ __forceinline__ void store_tile_lds(const floatx16_t (&acc)[4][4], fl
   }
 }
 
+// Workgroup b -> C tile (row-major tile index) for the 256 x 256 GEMM
+// tiles. Workgroups are handed to the 8 XCDs in turn (b % 8), and each XCD
+// has its own L2. When the tile grid divides into blocks of 32 tiles (4 tile
+// rows x 8 tile columns, else 8 x 4), the 32 workgroups an XCD runs side by
+// side take one block, so they read 12 operand panels between them (in
+// row-major order about 13, spread over several panel rows and, started at
+// different times, reused less from L2). Blocks are taken 8 at a time, one
+// per XCD, in row-major block order; blocks past the last full set of 8
+// follow in plain order. Other grids keep row-major order. A bijection on
+// [0, tiles_m * tiles_n).
+__device__ __forceinline__ int64_t tile_of(int64_t b, int64_t tiles_m, int64_t tiles_n) {
+  int bh, lw;  // block height in tile rows; log2 of its width
+  if ((tiles_m & 3) == 0 && (tiles_n & 7) == 0) {
+    bh = 4;
+    lw = 3;
+  } else if ((tiles_m & 7) == 0 && (tiles_n & 3) == 0) {
+    bh = 8;
+    lw = 2;
+  } else {
+    return b;
+  }
+  const int64_t blocks_n = tiles_n >> lw;
+  const int64_t blocks = (tiles_m / bh) * blocks_n;
+  const int64_t full = blocks & ~static_cast<int64_t>(7);
+  int64_t blk, i;
+  if (b < full * 32) {
+    const int64_t l = b >> 3;  // this XCD's l-th workgroup
+    blk = (l >> 5) * 8 + (b & 7);
+    i = l & 31;
+  } else {
+    blk = full + ((b - full * 32) >> 5);
+    i = (b - full * 32) & 31;
+  }
+  const int64_t bm = blk / blocks_n, bn = blk - bm * blocks_n;
+  return (bm * bh + (i >> lw)) * tiles_n + (bn << lw) + (i & ((1 << lw) - 1));
+}
+
 // Writes zeros to C (the K == 0 product).
 __global__ void zero_output_kernel(void* c, int64_t M, int64_t N, int64_t ldc, bool bf16);
 

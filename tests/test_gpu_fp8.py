@@ -150,10 +150,11 @@ def test_fp8_empty_and_non_finite():
 
 @pytest.mark.parametrize("m,n,k", [(32, 32, 64), (256, 256, 64), (300, 520, 128), (33, 47, 192),
                                    (512, 768, 1024), (2500, 2608, 512), (272, 256, 5120),
-                                   (3072, 6144, 128)])
+                                   (3072, 6144, 128), (4096, 5120, 128)])
 def test_fp8_gemm_parity(m, n, k):
     """(3072, 6144, 128): 12 x 24 tiles, nine 4 x 8 tile blocks: eight handed
-    to the XCDs together, one after them in plain order."""
+    to the XCDs together, one after them in plain order. (4096, 5120, 128):
+    16 x 20 tiles, ten 8 x 4 blocks."""
     torch = require_gpu()
     import bit_block_scaled_bf16_amd as nv
 

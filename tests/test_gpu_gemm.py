@@ -60,10 +60,15 @@ def check(c_gpu, ref, absref, k, bf16=True):
 # two full rounds; (4352, 8192, 384) two full rounds plus a last round of 32
 # tiles as quarters; (1024, 22784, 256) 356 tiles, a full round and a last
 # round of 100 tiles, too many for quarters.
+# Tile blocks per XCD (tile_of): (4096, 8192, 256) is 16 x 32 tiles, sixteen
+# 4 x 8 blocks; (3072, 6144, 256) 12 x 24 tiles, nine 4 x 8 blocks, the last
+# in plain order and run as quarters; (4096, 5120, 256) 16 x 20 tiles, ten
+# 8 x 4 blocks, the last two in plain order and run as quarters.
 @pytest.mark.parametrize("m,n,k", [(16, 16, 16), (256, 256, 64), (300, 520, 80), (512, 768, 1024),
                                    (33, 47, 208), (272, 256, 5120), (2500, 2608, 208),
                                    (4312, 4080, 336), (4100, 4080, 384), (4096, 8192, 256),
-                                   (4352, 8192, 384), (1024, 22784, 256)])
+                                   (4352, 8192, 384), (1024, 22784, 256), (3072, 6144, 256),
+                                   (4096, 5120, 256)])
 @pytest.mark.parametrize("b_2d", [False, True])
 def test_gemm_parity(m, n, k, b_2d):
     torch = require_gpu()
