@@ -3,64 +3,67 @@
 // gist.science summary of "Pretraining Large Language Models with NVFP4",
 // Resumen técnico §2 "Formato NVFP4".
 //
-// One thread expands one 16-element block: 8 code bytes and 1 scale byte in,
-// 64 (float32) or 32 (bf16) bytes out.
+// A wave expands 64 consecutive 16-byte pieces of one output row: 8 values
+// per lane for bf16 output, 4 for float32, so each store instruction writes
+// 1 KiB of contiguous output (whole 128-byte lines). A lane reads the 4 (or
+// 2) code bytes of its values and its block's scale byte. The E2M1 values
+// come from gfx950's FP4 -> float32 converter with scale 1.0 (exact), then
+// two float32 multiplies in the order of the definition; bf16 output is the
+// RNE of that float32, two values per conversion.
 #include "device_common.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace nvfp4 {
 namespace {
 
-// Value of a 4-bit E2M1 code from its bit fields.
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  const float mag = (e == 0u) ? 0.5f * static_cast<float>(m)
-                              : __uint_as_float(((e + 126u) << 23) | (m << 22));
-  return __uint_as_float(__float_as_uint(mag) | ((c & 8u) << 28));
-}
+using gemm_common::f32x2_to_bf16x2;
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t b = __float_as_uint(f);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;  // rows per workgroup (one per wave)
 
 template <bool kBlock2D, bool kBf16>
-__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ q,
-                                                         const uint8_t* __restrict__ sc,
-                                                         const float* __restrict__ tensor_scale,
-                                                         int64_t rows, int64_t cols, void* y,
-                                                         int64_t ldy) {
-  const int64_t nbc = cols >> 4;
-  const int64_t total = rows * nbc;
+__global__ __launch_bounds__(64 * kWaves) void dequantize_kernel(const uint8_t* __restrict__ q,
+                                                                 const uint8_t* __restrict__ sc,
+                                                                 const float* __restrict__ tensor_scale,
+                                                                 int64_t rows, int64_t cols, void* y,
+                                                                 int64_t ldy, int64_t chunks, int64_t units) {
+  constexpr int kPerLane = kBf16 ? 8 : 4;  // values per lane: 16 bytes of output
+  constexpr int kChunk = 64 * kPerLane;    // values per wave
   const float s = *tensor_scale;
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; b < total;
-       b += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t r = b / nbc, cb = b - r * nbc;
-    const uint2 codes = *reinterpret_cast<const uint2*>(q + r * (cols >> 1) + cb * 8);
-    const uint32_t sbyte = kBlock2D ? sc[(r >> 4) * nbc + cb] : sc[r * nbc + cb];
+  const int64_t nbc = cols >> 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // unit u: rows 4 (u / chunks) .. + 3, columns kChunk (u % chunks) .. + kChunk - 1
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t rg = u / chunks;
+    const int64_t row = rg * kWaves + wave;
+    const int64_t col = (u - rg * chunks) * kChunk + lane * kPerLane;
+    if (row >= rows || col >= cols) continue;
+    const uint32_t sbyte = kBlock2D ? sc[(row >> 4) * nbc + (col >> 4)] : sc[row * nbc + (col >> 4)];
     const float sf = e4m3_to_float(sbyte);
-    float out[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t word = (j < 8) ? codes.x : codes.y;
-      const uint32_t c = (word >> (4 * (j & 7))) & 0xFu;
-      out[j] = __fmul_rn(__fmul_rn(e2m1_value(c), sf), s);
-    }
+    const uint8_t* qp = q + row * (cols >> 1) + (col >> 1);
+    float v[kPerLane];
     if constexpr (kBf16) {
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + r * ldy + cb * 16);
-      uint32_t w[8];
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(qp);
+      const float2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+      const float2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+      const float2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+      const float2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+      const float e[8] = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        w[k] = f32_to_bf16_rne(out[2 * k]) | (f32_to_bf16_rne(out[2 * k + 1]) << 16);
-      }
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      for (int j = 0; j < 8; ++j) v[j] = __fmul_rn(__fmul_rn(e[j], sf), s);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + row * ldy + col) =
+          make_uint4(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]), f32x2_to_bf16x2(v[4], v[5]),
+                     f32x2_to_bf16x2(v[6], v[7]));
     } else {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(y) + r * ldy + cb * 16);
+      const uint32_t w = *reinterpret_cast<const uint16_t*>(qp);
+      const float2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+      const float2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+      const float e[4] = {p0[0], p0[1], p1[0], p1[1]};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        dst[k] = make_float4(out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]);
-      }
+      for (int j = 0; j < 4; ++j) v[j] = __fmul_rn(__fmul_rn(e[j], sf), s);
+      *reinterpret_cast<float4*>(static_cast<float*>(y) + row * ldy + col) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
 }
@@ -70,17 +73,18 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 int launch_dequantize(const uint8_t* q, const uint8_t* s, const float* tensor_scale, int64_t rows,
                       int64_t cols, bool block_2d, bool out_bf16, void* y, int64_t ldy,
                       hipStream_t stream) {
-  const int64_t total = rows * (cols >> 4);
-  if (total == 0) return 0;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  const unsigned g = static_cast<unsigned>(blocks);
+  if (rows == 0 || cols == 0) return 0;
+  const int64_t chunk = out_bf16 ? 512 : 256;
+  const int64_t chunks = (cols + chunk - 1) / chunk;
+  const int64_t units = ((rows + kWaves - 1) / kWaves) * chunks;
+  const unsigned g = static_cast<unsigned>(units < (int64_t(1) << 20) ? units : (int64_t(1) << 20));
+  const unsigned t = 64 * kWaves;
   if (block_2d) {
-    if (out_bf16) dequantize_kernel<true, true><<<g, 256, 0, stream>>>(q, s, tensor_scale, rows, cols, y, ldy);
-    else dequantize_kernel<true, false><<<g, 256, 0, stream>>>(q, s, tensor_scale, rows, cols, y, ldy);
+    if (out_bf16) dequantize_kernel<true, true><<<g, t, 0, stream>>>(q, s, tensor_scale, rows, cols, y, ldy, chunks, units);
+    else dequantize_kernel<true, false><<<g, t, 0, stream>>>(q, s, tensor_scale, rows, cols, y, ldy, chunks, units);
   } else {
-    if (out_bf16) dequantize_kernel<false, true><<<g, 256, 0, stream>>>(q, s, tensor_scale, rows, cols, y, ldy);
-    else dequantize_kernel<false, false><<<g, 256, 0, stream>>>(q, s, tensor_scale, rows, cols, y, ldy);
+    if (out_bf16) dequantize_kernel<false, true><<<g, t, 0, stream>>>(q, s, tensor_scale, rows, cols, y, ldy, chunks, units);
+    else dequantize_kernel<false, false><<<g, t, 0, stream>>>(q, s, tensor_scale, rows, cols, y, ldy, chunks, units);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

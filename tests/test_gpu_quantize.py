@@ -69,6 +69,43 @@ def test_fp32_outlier_matrix_rn_round_trip():
     assert np.array_equal(deq16, want16)
 
 
+# Dequantization on its own, from arbitrary stored bytes: every code pair and
+# every non-NaN scale byte (0x00 zero, 0x01-0x07 E4M3 subnormals) appear.
+# A wave covers 512 bf16 or 256 float32 values of a row; the shapes leave
+# partial pieces at row ends (400, 1040, 528 columns), row counts that are
+# not multiples of the workgroup's 4 rows (5, 33), and padded output rows.
+@pytest.mark.parametrize("rows,cols,block2d,pad", [(1, 16, False, 0), (5, 400, False, 8),
+                                                    (33, 1040, False, 0), (64, 528, True, 16),
+                                                    (48, 4096, True, 0), (256, 5120, False, 24)])
+@pytest.mark.parametrize("out", ["fp32", "bf16"])
+def test_dequantize_parity(rows, cols, block2d, pad, out):
+    torch = require_gpu()
+    import bit_block_scaled_bf16_amd as nv
+
+    announce(f"dequantize {rows}x{cols} 2d={block2d} pad={pad} {out}")
+    rng = np.random.default_rng(rows * 7 + cols)
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    sshape = (rows // 16, cols // 16) if block2d else (rows, cols // 16)
+    scales = rng.integers(0, 0x7F, size=sshape, dtype=np.uint8)  # 0x00 .. 0x7E
+    scales.flat[: min(8, scales.size)] = np.arange(min(8, scales.size), dtype=np.uint8)
+    ts = np.float32(0.37)
+    want = o.dequantize(codes, scales, ts, block="2d" if block2d else "1d")
+    dt = torch.float32 if out == "fp32" else torch.bfloat16
+    elem_pad = pad if out == "fp32" else 2 * pad  # keeps the row pitch a multiple of 16 bytes
+    full = torch.full((rows, cols + elem_pad), 7.0, dtype=dt, device="cuda")
+    y = full[:, :cols]
+    nv.nvfp4_dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                        torch.tensor([ts], device="cuda"), rows, cols,
+                        nv.BLOCK_2D if block2d else nv.BLOCK_1D, y)
+    got = host(full.float())
+    if out == "fp32":
+        assert np.array_equal(got[:, :cols].view(np.uint32), want.view(np.uint32))
+    else:
+        want16 = torch.from_numpy(want).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(got[:, :cols], want16)
+    assert np.all(got[:, cols:] == 7.0)  # the padding is untouched
+
+
 @pytest.mark.parametrize("shape", [(16, 16), (48, 160), (272, 400), (528, 272)])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_dual_rn_ragged_tiles(shape, dtype):
