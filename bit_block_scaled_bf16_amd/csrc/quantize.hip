@@ -60,21 +60,27 @@ struct Tile {
   bool valid;
 };
 
-__device__ __forceinline__ Tile locate_tile(int64_t tile, int64_t rows, int64_t cols) {
+__device__ __forceinline__ Tile locate_rc(int64_t tr, int64_t tc, int64_t rows, int64_t cols) {
   Tile t;
   const int tid = threadIdx.x;
   t.lane = tid & 63;
   t.wave = tid >> 6;
   t.cg = t.lane & 15;
   t.rg = t.lane >> 4;
-  const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
-  t.tr = tile / tiles_c;
-  t.tc = tile - t.tr * tiles_c;
+  t.tr = tr;
+  t.tc = tc;
   t.r0 = t.tr * kTileRows + t.wave * 64 + t.rg * 16;
   t.c0 = t.tc * kTileCols + t.cg * 8;
   t.valid = (t.r0 < rows) && (t.c0 < cols);
   t.nrows = (rows - t.r0) < 16 ? static_cast<int>(rows - t.r0) : 16;
   return t;
+}
+
+// Tile `tile` in row-major order.
+__device__ __forceinline__ Tile locate_tile(int64_t tile, int64_t rows, int64_t cols) {
+  const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
+  const int64_t tr = tile / tiles_c;
+  return locate_rc(tr, tile - tr * tiles_c, rows, cols);
 }
 
 // Workgroups are handed to the 8 XCDs of the chip round-robin (workgroup b
@@ -91,12 +97,34 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t ntiles) {
   return x * q + (x < r ? x : r) + j;
 }
 
-__device__ __forceinline__ Tile locate(int64_t rows, int64_t cols) {
-  const int64_t ntiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
-  return locate_tile(xcd_tile(static_cast<int64_t>(blockIdx.x), ntiles), rows, cols);
+// Tile k of the band order: bands of 8 tile rows, each walked column by
+// column (its 8 tiles down, then the next column). With xcd_tile handing
+// each XCD a contiguous run of this order, the 128-160 workgroups an XCD
+// runs at once cover about 16-20 columns x 8 rows of tiles. Every 128-byte
+// line of the row scales (8 bytes from each of 16 horizontally adjacent
+// tiles), of the column scales (16 bytes from each of 8 vertically adjacent
+// tiles) and of the row codes (two horizontal halves) is then written by
+// workgroups that run together behind one L2, which merges the pieces. A
+// permutation of [0, tiles_r * tiles_c).
+constexpr int64_t kBandRows = 8;
+
+__device__ __forceinline__ void band_tile(int64_t k, int64_t tiles_r, int64_t tiles_c, int64_t& tr,
+                                          int64_t& tc) {
+  const int64_t band = k / (kBandRows * tiles_c);
+  const int64_t tr0 = band * kBandRows;
+  const int64_t h = tiles_r - tr0 < kBandRows ? tiles_r - tr0 : kBandRows;
+  const int64_t kin = k - band * kBandRows * tiles_c;
+  tc = kin / h;
+  tr = tr0 + (kin - tc * h);
 }
 
-// Loads this lane's 16 x 8 values as float32 (bf16 widened exactly).
+__device__ __forceinline__ Tile locate(int64_t rows, int64_t cols) {
+  const int64_t tiles_r = (rows + kTileRows - 1) / kTileRows, tiles_c = (cols + kTileCols - 1) / kTileCols;
+  int64_t tr, tc;
+  band_tile(xcd_tile(static_cast<int64_t>(blockIdx.x), tiles_r * tiles_c), tiles_r, tiles_c, tr, tc);
+  return locate_rc(tr, tc, rows, cols);
+}
+
 // Loads this lane's 16 x 8 values as float32 (bf16 widened exactly). With
 // kRagged, rows at or beyond r0 + nrows (a row count that is not a multiple
 // of 16, allowed only for the row-blocked copy) read as zero; otherwise all
@@ -932,18 +960,22 @@ struct MfmaTile {
 // alone then has the workgroups that run together on an XCD (see xcd_tile)
 // write consecutive pieces of the same output rows (columns of x): its code
 // and scale bytes leave as longer runs, and the 16-byte scale pieces of one
-// 128-byte line meet in the L2. With a row copy too, row-major order does the
-// same for the row copy's half lines.
-template <bool kColMajor = false>
+// 128-byte line meet in the L2. With a row copy too, the band order (see
+// band_tile) does it for both copies' scale lines and the row copy's half
+// lines.
+enum class TileOrder { kRowMajor, kColMajor, kBand };
+
+template <TileOrder kOrder = TileOrder::kRowMajor>
 __device__ __forceinline__ MfmaTile locate_mfma(int64_t tile, int64_t rows, int64_t cols) {
   MfmaTile t;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if constexpr (kColMajor) {
-    const int64_t tiles_r = (rows + kTileRows - 1) / kTileRows;
+  const int64_t tiles_r = (rows + kTileRows - 1) / kTileRows, tiles_c = (cols + kTileCols - 1) / kTileCols;
+  if constexpr (kOrder == TileOrder::kColMajor) {
     t.tc = tile / tiles_r;
     t.tr = tile - t.tc * tiles_r;
+  } else if constexpr (kOrder == TileOrder::kBand) {
+    band_tile(tile, tiles_r, tiles_c, t.tr, t.tc);
   } else {
-    const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
     t.tr = tile / tiles_c;
     t.tc = tile - t.tr * tiles_c;
   }
@@ -1152,7 +1184,8 @@ __global__ __launch_bounds__(kThreads) void rht_quantize_mfma_kernel(QuantParams
   __shared__ float rtab_r[kDual ? 128 : 1];
   const int64_t rows = p.rows, cols = p.cols;
   const int64_t ntiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
-  const MfmaTile t = locate_mfma<!kDual>(xcd_tile(static_cast<int64_t>(blockIdx.x), ntiles), rows, cols);
+  constexpr TileOrder kOrder = kDual ? TileOrder::kBand : TileOrder::kColMajor;
+  const MfmaTile t = locate_mfma<kOrder>(xcd_tile(static_cast<int64_t>(blockIdx.x), ntiles), rows, cols);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, r = lane >> 4;
   const uint16_t* x = static_cast<const uint16_t*>(p.x);
