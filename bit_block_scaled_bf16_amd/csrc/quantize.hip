@@ -924,6 +924,33 @@ __device__ __forceinline__ uint32_t word_of(const uint4& r) {
 // each): the j-th bf16 of every row, paired into the B operand by two byte
 // permutes, then one MFMA. Result v = token 4 (l / 16) + v of column j.
 template <int j>
+__device__ __forceinline__ u32x2_t rht_b_operand(const uint4* rows4) {
+  constexpr uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+  const uint32_t lo = __builtin_amdgcn_perm(word_of<j / 2>(rows4[1]), word_of<j / 2>(rows4[0]), sel);
+  const uint32_t hi = __builtin_amdgcn_perm(word_of<j / 2>(rows4[3]), word_of<j / 2>(rows4[2]), sel);
+  return u32x2_t{lo, hi};
+}
+
+// Columns j0 .. j0 + 3 in one block: the results land in VGPRs that do not
+// overlap the sources (early-clobber), with the wait states around the four
+// MFMAs written out (2 before for the B operands' producers, 16 after for the
+// readers of the results).
+template <int j0>
+__device__ __forceinline__ void rht_mfma4(bf16x4_t a, const uint4* rows4, f32x4_t (&o)[4]) {
+  const u32x2_t b0 = rht_b_operand<j0>(rows4), b1 = rht_b_operand<j0 + 1>(rows4);
+  const u32x2_t b2 = rht_b_operand<j0 + 2>(rows4), b3 = rht_b_operand<j0 + 3>(rows4);
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_16x16x16_bf16 %0, %4, %5, 0\n\t"
+      "v_mfma_f32_16x16x16_bf16 %1, %4, %6, 0\n\t"
+      "v_mfma_f32_16x16x16_bf16 %2, %4, %7, 0\n\t"
+      "v_mfma_f32_16x16x16_bf16 %3, %4, %8, 0\n\t"
+      "s_nop 7\n\ts_nop 7"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(a), "v"(b0), "v"(b1), "v"(b2), "v"(b3));
+}
+
+template <int j>
 __device__ __forceinline__ f32x4_t rht_mfma(bf16x4_t a, const uint4* rows4) {
   constexpr uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
   const uint32_t lo = __builtin_amdgcn_perm(word_of<j / 2>(rows4[1]), word_of<j / 2>(rows4[0]), sel);
@@ -1288,15 +1315,10 @@ __global__ __launch_bounds__(kThreads) void rht_quantize_mfma_kernel(QuantParams
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x4_t o[4];
-      o[0] = rht_mfma<0>(a, rs);
-      o[1] = rht_mfma<1>(a, rs);
-      o[2] = rht_mfma<2>(a, rs);
-      o[3] = rht_mfma<3>(a, rs);
-      if (h == 1) {
-        o[0] = rht_mfma<4>(a, rs);
-        o[1] = rht_mfma<5>(a, rs);
-        o[2] = rht_mfma<6>(a, rs);
-        o[3] = rht_mfma<7>(a, rs);
+      if (h == 0) {
+        rht_mfma4<0>(a, rs, o);
+      } else {
+        rht_mfma4<4>(a, rs, o);
       }
       // block maxima over the columns' 4 lanes (rows r of the lane grid):
       // after the two swaps, lane row r holds column {0, 2, 1, 3}[r] of the four
