@@ -106,7 +106,9 @@ def test_dequantize_parity(rows, cols, block2d, pad, out):
     assert np.all(got[:, cols:] == 7.0)  # the padding is untouched
 
 
-@pytest.mark.parametrize("shape", [(16, 16), (48, 160), (272, 400), (528, 272)])
+# (2320, 400): 10 tile rows, i.e. a full band of 8 and a band of 2 whose
+# last tile is ragged (tiles go to the XCDs in bands walked column by column)
+@pytest.mark.parametrize("shape", [(16, 16), (48, 160), (272, 400), (528, 272), (2320, 400)])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_dual_rn_ragged_tiles(shape, dtype):
     announce(f"dual RN {shape} {dtype}")
@@ -209,7 +211,7 @@ def test_caller_supplied_amax():
     check_against_oracle(x, "bf16", amax=a / 3)
 
 
-@pytest.mark.parametrize("shape", [(16, 16), (272, 400), (512, 384)])
+@pytest.mark.parametrize("shape", [(16, 16), (272, 400), (512, 384), (2320, 384)])
 def test_2d_weight_blocks(shape):
     announce(f"2D {shape}")
     x = wl.weight(*shape, seed=4)

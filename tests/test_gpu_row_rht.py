@@ -156,6 +156,7 @@ def _check_hadamard_copy(x_np, x, col, ws, rounding, seed, offset):
 @pytest.mark.parametrize("rounding", [0, 1])
 @pytest.mark.parametrize("shape,dtype", [((16, 16), "bf16"), ((272, 400), "bf16"),
                                          ((528, 272), "bf16"), ((1040, 2064), "bf16"),
+                                         ((2320, 400), "bf16"),
                                          ((272, 400), "fp32"), ((528, 144), "fp32")])
 def test_hadamard_copy_against_oracle(shape, dtype, rounding):
     announce(f"row+rht hadamard copy vs oracle {shape} {dtype} r={rounding}")
