@@ -24,6 +24,11 @@
 // exact). Keeping the codes, not fp16 values, in LDS moves a quarter of the
 // bytes through it.
 //
+// Tile order and epilogue. Tiles go to the XCDs in blocks of 32 that share
+// operand panels (tile_of, gemm_common.h). A wave writes its 128 x 128
+// results through LDS as whole 128-byte lines of C, with nontemporal stores
+// (store_tile_lds); edge tiles store 8-byte pieces.
+//
 // Last round. 256 x 256 tiles keep one workgroup per CU busy; when the tile
 // count leaves a last round that fills at most a quarter of the CUs, those
 // tiles are computed as four 128 x 128 tiles each (the same kernel with

@@ -9,10 +9,14 @@
 // Bidimensional (2D) y Redondeo Estocástico" (16x16 weight tiles; stochastic
 // rounding of gradients).
 //
-// Two quantize kernels. A call that asks for the 1x16 row copy alone goes
-// through quantize_rows_kernel (see its comment), which streams rows. Every
-// other call (a column copy, both copies, 16x16 blocks, the Hadamard path)
-// goes through quantize_kernel, whose decomposition follows.
+// Three quantize kernels. A call that asks for the 1x16 row copy alone goes
+// through quantize_rows_kernel (see its comment), which streams rows. The
+// Hadamard path of bf16 input (alone, or with the 1x16 row copy from the
+// same read) goes through rht_quantize_mfma_kernel, which transforms on the
+// matrix cores (see "The Hadamard path of bf16 inputs on the matrix cores").
+// Every other call (a column copy, both copies, 16x16 blocks, the Hadamard
+// path of float32 input) goes through quantize_kernel, whose decomposition
+// follows; the MFMA kernel keeps its 256 x 128 tile and its LDS staging.
 //
 // Work decomposition. A workgroup of 256 threads (4 waves) owns a tile of
 // 256 rows x 128 columns. Lane l of wave w owns the 16 rows starting at
